@@ -1,0 +1,312 @@
+"""Benchmark of the fused W-way reduce + residual add + RMSNorm (libarrms).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--full PATH] [--copy-calibration]
+
+Workload of the headline line: the decode-window sweep, W=4 partial buffers of
+[T, 4096] bf16 with Gemma RMSNorm, eps 1e-6, T in {1, 2, 4, 8, 16, 21, 22, 32,
+64, 80}, row-resident kernel.  One step is one pass over the sweep: ten fused
+calls, one per T, replayed from a HIP graph; inputs are resident in HBM before
+the timed region starts.  value = microseconds per fused call (step time / 10).
+
+The roofline object covers the dominant kernel (the row-resident kernel, every
+launch of the step): algorithmic bytes per launch, (W + 2) * T * H * 2 + H * 2
+averaged over the sweep, divided by that kernel's average launch duration,
+measured with HIP events on the stream the graph is replayed on.  `traffic` is
+read from the committed rocprofv3 counter summary when it was taken on the
+current kernel source, else null.
+
+cpu_baseline: the oracle, single-threaded, on the same sweep, repeated for
+about 10 s on the host.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = ("µs/call at T<=80 and effective HBM GB/s (% of MI355X peak) for W-way "
+          "reduce+add-RMSNorm")
+KERNEL_SRC = os.path.join(ROOT, "tp_all_reduce_amd", "csrc", "arrms.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_kernel_c2_sweep.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--full", default=None,
+                    help="also time every workload (c1..c5) and write a JSON report here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--only", default=None, choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="with --full: time only this workload (profiling runs)")
+    return ap.parse_args()
+
+
+def to_dev(d, dev):
+    return {k: ([x.to(dev) for x in v] if isinstance(v, list) else
+                (None if v is None else v.to(dev))) for k, v in d.items()}
+
+
+def graph_time(torch, launch, reps, warmup, calls_per_rep, stream):
+    """Captures `launch()` (which queues `calls_per_rep` library calls on
+    `stream`) in a HIP graph and returns (us per call, total elapsed ms) over
+    `reps` replays timed with HIP events on the replaying stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        launch()                      # eager warm-up of the same calls
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            launch()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    end.synchronize()
+    ms = start.elapsed_time(end)
+    return ms * 1000.0 / (reps * calls_per_rep), ms
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library is the single-GPU kernel of the "
+              "fused all-reduce + RMSNorm epilogue (W partial buffers resident on one device); "
+              "multi-GPU runs are not part of it. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tp_all_reduce_amd import arrms, workloads
+    from tp_all_reduce_amd.workloads import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    arrms.library()   # fails loudly if the HIP library is not built
+
+    if args.copy_calibration:
+        n = 256 * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
+
+    wl = WORKLOADS["c2"]
+    Ts = wl.Ts
+    log(f"[bench] building inputs: c2 W={wl.W} H={wl.H} T={list(Ts)}")
+    cases = []
+    for T in Ts:
+        inp = to_dev(workloads.make_inputs(wl, T), dev)
+        plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16, arrms.FORCE_ROW)
+        norm = torch.empty_like(inp["partials"][0])
+        res = torch.empty_like(inp["residual"])
+        cases.append((T, inp, plan, norm, res))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+
+    def step():
+        for T, inp, plan, norm, res in cases:
+            arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
+                             True, norm, res, stream=stream)
+
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps")
+    us_per_call, ms_total = graph_time(torch, step, args.steps, args.warmup, len(Ts), stream)
+    ms_per_step = ms_total / args.steps
+    H, W = wl.H, wl.W
+    bytes_per_launch = sum((W + 2) * T * H * 2 + H * 2 for T in Ts) / len(Ts)
+    achieved = bytes_per_launch / (us_per_call * 1e-6) / 1e9
+    log(f"[bench] {us_per_call:.3f} us/call (graph), {achieved:.1f} GB/s algorithmic")
+
+    # per-T detail (same graph method, one T at a time)
+    per_t = {}
+    for case in cases:
+        T, inp, plan, norm, res = case
+
+        def one(case=case):
+            T_, inp_, plan_, norm_, res_ = case
+            for _ in range(20):
+                arrms.ar_rms_run(plan_, inp_["partials"], inp_["residual"], inp_["weight"],
+                                 wl.eps, True, norm_, res_, stream=stream)
+        us, _ = graph_time(torch, one, 50, 5, 20, stream)
+        per_t[str(T)] = round(us, 3)
+    log(f"[bench] per-T us/call: {per_t}")
+
+    # launch floor on this machine: a one-element torch fill kernel replayed the
+    # same way (what any single-kernel call costs before it does any work)
+    tiny = torch.zeros(1, device=dev)
+
+    def fill():
+        for _ in range(20):
+            tiny.fill_(1.0)
+    floor_us, _ = graph_time(torch, fill, 50, 5, 20, stream)
+    log(f"[bench] launch floor (1-element fill kernel, graph): {floor_us:.3f} us")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("kernel_source_sha") == kernel_source_sha():
+            traffic = rec.get("traffic_bytes_per_launch")
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
+                "kernel": "reduce_norm_kernel<Bf16, W=4, 1 pack/lane, no prefetch> (row-resident)",
+                "bytes_per_launch": bytes_per_launch, "us_per_launch": round(us_per_call, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cases, wl, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu}")
+
+    secondary = {}
+    if args.full:
+        secondary = full_report(torch, arrms, workloads, WORKLOADS, dev, stream, args)
+        with open(args.full, "w") as f:
+            json.dump({"c2_sweep": {"us_per_call": us_per_call, "per_T": per_t},
+                       "workloads": secondary}, f, indent=1)
+
+    line = {
+        "metric": METRIC, "value": round(us_per_call, 4), "unit": "µs/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c2 decode sweep: W=4 partials [T,4096] bf16, Gemma RMSNorm, "
+                               "eps 1e-6, T in {1,2,4,8,16,21,22,32,64,80}, row-resident kernel; "
+                               "one step = 10 fused calls replayed from a HIP graph",
+                   "W": W, "H": H, "T": list(Ts), "calls_per_step": len(Ts),
+                   "per_T_us_per_call": per_t,
+                   "launch_floor_us": round(floor_us, 3)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cases, wl, seconds):
+    """The oracle as it stands, single-threaded, on the same sweep."""
+    import numpy as np
+    import oracle
+    from oracle import compare
+    from tp_all_reduce_amd.workloads import bits
+
+    host = [([bits(p) for p in inp["partials"]], bits(inp["residual"]), bits(inp["weight"]),
+             norm, res) for T, inp, plan, norm, res in cases]
+    # the sample's GPU outputs must match the oracle (parity guard of the bench)
+    for P, R, w, norm, res in host:
+        n_o, r_o, exact = oracle.ar_rms(P, R, w, wl.eps, True)
+        assert compare.bits_equal(bits(res), r_o)
+        assert compare.max_relerr(bits(norm), exact, oracle.BF16) <= compare.TOL[oracle.BF16]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for P, R, w, _, _ in host:
+            oracle.ar_rms(P, R, w, wl.eps, True, want_exact=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    us = el * 1e6 / (reps * len(host))
+    del np
+    return {"value": round(us, 2), "unit": "µs/call", "cores": 1, "kind": "oracle",
+            "sample": f"the full c2 sweep (10 calls, T=1..80) repeated {reps} times "
+                      f"({el:.1f} s, one thread)"}
+
+
+def full_report(torch, arrms, workloads, WORKLOADS, dev, stream, args):
+    """Times every workload with the graph method; bytes are algorithmic."""
+    out = {}
+    todo = [args.only] if args.only else ["c1", "c3", "c4", "c5"]
+    for name in todo:
+        wl = WORKLOADS[name]
+        for T in wl.Ts:
+            key = f"{name}_T{T}"
+            log(f"[bench] {key}")
+            if name == "c5":
+                inp = to_dev(workloads.make_qk_inputs(wl, T), dev)
+                plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16)
+                qo = torch.empty((wl.W, T, wl.q_size), dtype=torch.bfloat16, device=dev)
+                ko = torch.empty((wl.W, T, wl.kv_size), dtype=torch.bfloat16, device=dev)
+
+                def call(inp=inp, plan=plan, qo=qo, ko=ko, wl=wl):
+                    for _ in range(20):
+                        arrms.ar_qknorm_run(plan, inp["shards"], wl.q_size, wl.kv_size,
+                                            inp["q_weight"], inp["k_weight"], wl.eps, qo, ko,
+                                            stream=stream)
+                nbytes = 2 * wl.W * T * (wl.q_size + wl.kv_size) * 2 + \
+                    wl.W * (wl.q_size + wl.kv_size) * 2
+                reps, n_calls = 50, 20
+            else:
+                big = T * wl.H * (wl.W + 2) * 2 > (1 << 29)
+                sets = 1 if big else 3
+                inps = []
+                for s in range(sets):
+                    seed = workloads.seed_of(wl, T) + 100000 * s
+                    inps.append(workloads.make_inputs(wl, T, device=dev, seed=seed))
+                plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16)
+                norm = torch.empty_like(inps[0]["partials"][0])
+                res = torch.empty_like(norm)
+                quant = wl.group > 0
+                if quant:
+                    q = torch.empty(norm.shape, dtype=torch.uint8, device=dev)
+                    sc = torch.empty((T, wl.H // wl.group), dtype=torch.float32, device=dev)
+                n_calls = 2 if big else 20
+
+                def call(inps=inps, plan=plan, norm=norm, res=res, wl=wl, quant=quant,
+                         n_calls=n_calls):
+                    for i in range(n_calls):
+                        inp = inps[i % len(inps)]
+                        if quant:
+                            arrms.ar_rms_quant_run(plan, inp["partials"], inp["residual"],
+                                                   inp["weight"], wl.eps, wl.gemma, wl.group,
+                                                   norm, q, sc, res, stream=stream)
+                        else:
+                            arrms.ar_rms_run(plan, inp["partials"], inp["residual"],
+                                             inp["weight"], wl.eps, wl.gemma, norm, res,
+                                             stream=stream)
+                nbytes = (wl.W + 2) * T * wl.H * 2 + wl.H * 2
+                if quant:
+                    nbytes += T * wl.H + 4 * T * (wl.H // wl.group)
+                reps = 10 if big else 50
+            us, _ = graph_time(torch, call, reps, 2, n_calls, stream)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[key] = {"us_per_call": round(us, 3), "bytes": nbytes, "GB_s": round(gbs, 1),
+                        "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                        "kernel": "row" if plan.kernel == 0 else "split"}
+            log(f"[bench]   {out[key]}")
+            del call
+            torch.cuda.empty_cache()
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -146,17 +146,17 @@ def one_stage(W: int, numel: int, hidden: int, fmt: int, fully_connected: int = 
 
 def ar_rms(partials, residual, weight, eps: float, gemma: bool, fmt: int = BF16,
            want_exact: bool = True):
-    """Returns (norm_out bits, residual_out bits or None, exact fp64 or None).
+    """Returns (norm_out bits, residual_out bits, exact fp64 or None).
 
-    partials: sequence of W uint16 arrays [T, H]; residual: [T, H] or None;
-    weight: [H]."""
+    partials: sequence of W uint16 arrays [T, H]; residual: [T, H] or None (no
+    residual term; residual_out is then the reduced sum itself); weight: [H]."""
     partials = [_u16(p) for p in partials]
     W = len(partials)
     T, H = partials[0].shape
     residual = None if residual is None else _u16(residual)
     weight = _u16(weight)
     norm = np.empty((T, H), np.uint16)
-    res_out = None if residual is None else np.empty((T, H), np.uint16)
+    res_out = np.empty((T, H), np.uint16)
     exact = np.empty((T, H), np.float64) if want_exact else None
     rc = _load().oracle_ar_rms(W, T, H, fmt, _ptr_array(partials),
                                _ptr(residual, ctypes.c_uint16), _ptr(weight, ctypes.c_uint16),
@@ -169,7 +169,7 @@ def ar_rms(partials, residual, weight, eps: float, gemma: bool, fmt: int = BF16,
 
 def ar_rms_quant(partials, residual, weight, eps: float, gemma: bool, group: int,
                  fmt: int = BF16, want_exact: bool = True):
-    """Returns (norm_out bits, codes u8, scales f32, residual_out bits or None, exact)."""
+    """Returns (norm_out bits, codes u8, scales f32, residual_out bits, exact)."""
     partials = [_u16(p) for p in partials]
     W = len(partials)
     T, H = partials[0].shape
@@ -178,7 +178,7 @@ def ar_rms_quant(partials, residual, weight, eps: float, gemma: bool, group: int
     norm = np.empty((T, H), np.uint16)
     codes = np.empty((T, H), np.uint8)
     scales = np.empty((T, H // group if group > 0 else 0), np.float32)
-    res_out = None if residual is None else np.empty((T, H), np.uint16)
+    res_out = np.empty((T, H), np.uint16)
     exact = np.empty((T, H), np.float64) if want_exact else None
     rc = _load().oracle_ar_rms_quant(W, T, H, fmt, _ptr_array(partials),
                                      _ptr(residual, ctypes.c_uint16),

@@ -1,0 +1,367 @@
+"""GPU parity of libarrms against the oracle, through the C ABI (via the ctypes
+binding), on seeded synthetic inputs.
+
+Small cases compare every output; the full-size workloads compare every row
+that the oracle can afford (all of them up to a few million elements, else a
+seeded sample of rows, rows being independent).  Acceptance (oracle/compare.py):
+residual_out bit-exact; norm_out and q/k outputs within 4e-3 (bf16) / 1e-3
+(fp16) relative to the oracle's fp64 value; FP8 codes within one step; FP8
+scales within 1e-6."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import compare
+from tp_all_reduce_amd import arrms, workloads
+from tp_all_reduce_amd.workloads import WORKLOADS, bits
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+FMT = {torch.bfloat16: oracle.BF16, torch.float16: oracle.FP16}
+
+
+def sample_rows(T, n=192, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
+    return np.unique(np.concatenate([[0, T - 1], pick]))
+
+
+def host_rows(t, rows):
+    idx = torch.as_tensor(rows, device=t.device, dtype=torch.long)
+    return bits(t.reshape(-1, t.shape[-1]).index_select(0, idx))
+
+
+def check_rms(inp, norm_out, residual_out, eps, gemma, rows=None, fmt=oracle.BF16,
+              expect_residual=True):
+    """Compares the GPU outputs with the oracle on `rows` (default: all)."""
+    T = inp["partials"][0].reshape(-1, inp["partials"][0].shape[-1]).shape[0]
+    rows = np.arange(T) if rows is None else rows
+    P = [host_rows(p, rows) for p in inp["partials"]]
+    R = None if inp["residual"] is None else host_rows(inp["residual"], rows)
+    n, r, exact = oracle.ar_rms(P, R, bits(inp["weight"]), eps, gemma, fmt)
+    err = compare.max_relerr(host_rows(norm_out, rows), exact, fmt)
+    assert err <= compare.TOL[fmt], f"norm_out relerr {err}"
+    if expect_residual:
+        res_gpu = host_rows(residual_out, rows)
+        assert compare.bits_equal(res_gpu, r), "residual_out differs from the oracle"
+    return err
+
+
+def run_rms(inp, eps, gemma, flags=0, residual_out="new"):
+    return arrms.fused_allreduce_rms_norm(inp["partials"], inp["residual"], inp["weight"], eps,
+                                          gemma, residual_out=residual_out, flags=flags)
+
+
+def cuda_inputs(wl, T, dtype=torch.bfloat16, device_draw=False, **kw):
+    if device_draw:
+        return workloads.make_inputs(wl, T, dtype, device=DEV, **kw)
+    inp = workloads.make_inputs(wl, T, dtype, device="cpu", **kw)
+    return {k: ([x.to(DEV) for x in v] if isinstance(v, list) else v.to(DEV))
+            for k, v in inp.items()}
+
+
+# ------------------------------------------------------------ the workloads
+def test_c1_decode_w2():
+    wl = WORKLOADS["c1"]
+    inp = cuda_inputs(wl, 8)
+    plan = arrms.cached_plan(wl.W, 8, wl.H, arrms.BF16)
+    assert plan.kernel == arrms.KERNEL_ROW
+    norm, res = run_rms(inp, wl.eps, wl.gemma)
+    torch.cuda.synchronize()
+    check_rms(inp, norm, res, wl.eps, wl.gemma)
+
+
+@pytest.mark.parametrize("flags", [arrms.FORCE_ROW, 0, arrms.FORCE_SPLIT],
+                         ids=["row", "default", "split"])
+@pytest.mark.parametrize("T", WORKLOADS["c2"].Ts)
+def test_c2_gemma_decode_sweep(T, flags):
+    wl = WORKLOADS["c2"]
+    inp = cuda_inputs(wl, T)
+    norm, res = run_rms(inp, wl.eps, True, flags=flags)
+    torch.cuda.synchronize()
+    check_rms(inp, norm, res, wl.eps, True)
+
+
+@pytest.mark.parametrize("T", WORKLOADS["c3"].Ts)
+def test_c3_prefill_w8(T):
+    wl = WORKLOADS["c3"]
+    inp = cuda_inputs(wl, T, device_draw=True)
+    plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16)
+    assert plan.kernel == arrms.KERNEL_SPLIT
+    norm, res = run_rms(inp, wl.eps, wl.gemma)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 1024 else sample_rows(T, 256, seed=T)
+    check_rms(inp, norm, res, wl.eps, wl.gemma, rows=rows)
+
+
+def check_quant(inp, eps, gemma, group, outs, rows=None, fmt=oracle.BF16):
+    norm, q, scales, res = outs
+    T = inp["partials"][0].shape[0]
+    rows = np.arange(T) if rows is None else rows
+    P = [host_rows(p, rows) for p in inp["partials"]]
+    R = None if inp["residual"] is None else host_rows(inp["residual"], rows)
+    n_o, c_o, s_o, r_o, exact = oracle.ar_rms_quant(P, R, bits(inp["weight"]), eps, gemma, group,
+                                                    fmt)
+    q_gpu = q.view(torch.uint8).reshape(T, -1)[torch.as_tensor(rows, device=q.device)].cpu().numpy()
+    s_gpu = scales.reshape(T, -1)[torch.as_tensor(rows, device=q.device)].cpu().numpy()
+    assert compare.max_code_distance(q_gpu, c_o) <= 1
+    assert compare.max_scale_relerr(s_gpu, s_o) <= compare.SCALE_TOL
+    if norm is not None:
+        assert compare.max_relerr(host_rows(norm, rows), exact, fmt) <= compare.TOL[fmt]
+    if res is not None:
+        assert compare.bits_equal(host_rows(res, rows), r_o)
+    return float(np.mean(q_gpu != c_o))
+
+
+def test_c4_fp8_group_quant():
+    wl = WORKLOADS["c4"]
+    inp = cuda_inputs(wl, 256)
+    outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"], inp["weight"],
+                                                wl.eps, wl.group)
+    torch.cuda.synchronize()
+    mismatch = check_quant(inp, wl.eps, False, wl.group, outs)
+    assert mismatch < 0.01      # almost every code identical; the rest one step away
+
+
+def check_qk(inp, q_size, kv_size, eps, q_out, k_out, fmt=oracle.BF16):
+    qo, ko, qe, ke = oracle.qknorm([bits(s) for s in inp["shards"]], q_size, kv_size,
+                                   bits(inp["q_weight"]), bits(inp["k_weight"]), eps, fmt)
+    eq = compare.max_relerr(bits(q_out), qe, fmt)
+    ek = compare.max_relerr(bits(k_out), ke, fmt)
+    assert eq <= compare.TOL[fmt] and ek <= compare.TOL[fmt], (eq, ek)
+
+
+def test_c5_qk_norm():
+    wl = WORKLOADS["c5"]
+    inp = workloads.make_qk_inputs(wl, 64)
+    inp = {k: ([x.to(DEV) for x in v] if isinstance(v, list) else v.to(DEV)) for k, v in inp.items()}
+    q_out, k_out = arrms.fused_qk_norm(inp["shards"], inp["q_weight"], inp["k_weight"],
+                                       wl.q_size, wl.kv_size, wl.eps)
+    torch.cuda.synchronize()
+    check_qk(inp, wl.q_size, wl.kv_size, wl.eps, q_out, k_out)
+
+
+# ------------------------------------------------- shapes: tiles and tails
+GENERIC = workloads.Workload("generic", 9, W=1, H=8, Ts=(1,), eps=1e-6)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("W,T,H", [(1, 1, 8), (3, 5, 72), (2, 37, 1000), (8, 3, 8192),
+                                   (5, 17, 2056), (7, 9, 4104), (4, 70, 16384), (2, 300, 1024),
+                                   (6, 129, 3000)])
+@pytest.mark.parametrize("flags", [0, arrms.FORCE_SPLIT], ids=["default", "split"])
+def test_generic_shapes(W, T, H, dtype, flags):
+    inp = cuda_inputs(GENERIC, T, dtype, W=W, H=H, seed=W * 7919 + T * 31 + H)
+    norm, res = run_rms(inp, 1e-5, False, flags=flags)
+    torch.cuda.synchronize()
+    check_rms(inp, norm, res, 1e-5, False, fmt=FMT[dtype])
+
+
+@pytest.mark.parametrize("W,T,H", [(2, 80, 8192), (1, 1, 8), (8, 13, 1096), (4, 31, 4096)])
+def test_row_kernel_shapes(W, T, H):
+    inp = cuda_inputs(GENERIC, T, W=W, H=H, seed=W + T + H)
+    norm, res = run_rms(inp, 1e-6, True, flags=arrms.FORCE_ROW)
+    torch.cuda.synchronize()
+    check_rms(inp, norm, res, 1e-6, True)
+
+
+@pytest.mark.parametrize("group", [8, 32, 64, 128, 256, 512])
+@pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
+def test_quant_group_sizes(group, flags):
+    W, T, H = 3, 11, 4096
+    inp = cuda_inputs(WORKLOADS["c4"], T, W=W, H=H, seed=group)
+    outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"], inp["weight"],
+                                                1e-6, group, flags=flags)
+    torch.cuda.synchronize()
+    check_quant(inp, 1e-6, False, group, outs)
+
+
+def test_quant_fp16_gemma_codes_only():
+    W, T, H = 2, 40, 2048
+    inp = cuda_inputs(WORKLOADS["c4"], T, torch.float16, W=W, H=H, seed=5)
+    outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"], inp["weight"],
+                                                1e-6, 128, gemma=True, with_norm=False)
+    torch.cuda.synchronize()
+    assert outs[0] is None
+    check_quant(inp, 1e-6, True, 128, outs, fmt=oracle.FP16)
+
+
+@pytest.mark.parametrize("W,T,q,kv", [(1, 3, 256, 256), (2, 17, 512, 256), (8, 5, 1024, 256),
+                                      (4, 130, 1536, 256), (3, 7, 2048, 512)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+def test_qk_shapes(W, T, q, kv, dtype):
+    inp = workloads.make_qk_inputs(WORKLOADS["c5"], T, dtype, W=W, q_size=q, kv_size=kv,
+                                   seed=W * 13 + T)
+    inp = {k: ([x.to(DEV) for x in v] if isinstance(v, list) else v.to(DEV)) for k, v in inp.items()}
+    q_out, k_out = arrms.fused_qk_norm(inp["shards"], inp["q_weight"], inp["k_weight"], q, kv,
+                                       1e-6)
+    torch.cuda.synchronize()
+    check_qk(inp, q, kv, 1e-6, q_out, k_out, FMT[dtype])
+
+
+# ------------------------------------------------------------- edge cases
+def test_zero_tokens_touch_nothing():
+    x = torch.empty(0, 1024, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(1024, dtype=torch.bfloat16, device=DEV)
+    norm, res = arrms.fused_allreduce_rms_norm([x, x], x, w, 1e-6)
+    torch.cuda.synchronize()
+    assert norm.shape == (0, 1024) and res.shape == (0, 1024)
+
+
+def test_three_d_input_tokens_are_numel_over_h():
+    wl = WORKLOADS["c2"]
+    inp = cuda_inputs(wl, 82)
+    inp3 = {"partials": [p.reshape(2, 41, wl.H) for p in inp["partials"]],
+            "residual": inp["residual"].reshape(2, 41, wl.H), "weight": inp["weight"]}
+    norm, res = run_rms(inp3, wl.eps, True)
+    torch.cuda.synchronize()
+    assert norm.shape == (2, 41, wl.H)
+    # 82 tokens: outside the one-stage window, so the split kernel ran
+    assert arrms.cached_plan(wl.W, 82, wl.H, arrms.BF16).kernel == arrms.KERNEL_SPLIT
+    check_rms(inp, norm.reshape(82, -1), res.reshape(82, -1), wl.eps, True)
+
+
+@pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
+def test_no_residual_and_dead_residual(flags):
+    wl = WORKLOADS["c2"]
+    inp = cuda_inputs(wl, 16)
+    # no residual term: residual_out (if requested) is the reduced sum itself
+    no_res = dict(inp, residual=None)
+    norm, red = run_rms(no_res, wl.eps, True, flags=flags)
+    torch.cuda.synchronize()
+    check_rms(no_res, norm, red, wl.eps, True)
+    # dead residual output: only norm_out is written
+    norm2, none = run_rms(inp, wl.eps, True, flags=flags, residual_out=None)
+    torch.cuda.synchronize()
+    assert none is None
+    check_rms(inp, norm2, None, wl.eps, True, expect_residual=False)
+
+
+@pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
+def test_residual_in_place(flags):
+    wl = WORKLOADS["c2"]
+    inp = cuda_inputs(wl, 21)
+    ref_inp = dict(inp, residual=inp["residual"].clone())
+    norm, res = run_rms(inp, wl.eps, True, flags=flags, residual_out=inp["residual"])
+    torch.cuda.synchronize()
+    assert res.data_ptr() == inp["residual"].data_ptr()
+    check_rms(ref_inp, norm, res, wl.eps, True)
+
+
+def test_rounding_ties_and_subnormals_bit_exact():
+    # fp32 sums landing exactly halfway between 16-bit neighbours, and sums in
+    # the subnormal range, decided by the oracle's nearest-even rounding
+    H, T = 1024, 4
+    for dtype, mant in ((torch.bfloat16, 7), (torch.float16, 10)):
+        rng = np.random.default_rng(7)
+        e = rng.integers(-12, 12, (T, H)).astype(np.float64)
+        if dtype == torch.float16:
+            e = np.clip(e, -12, 12)
+        m = rng.integers(1 << mant, 1 << (mant + 1), (T, H)).astype(np.float64)
+        a = m * np.exp2(e - mant)                         # exactly representable
+        half_ulp = np.exp2(e - mant - 1) * np.where(rng.random((T, H)) < 0.5, 1, -1)
+        tiny = np.exp2(-130.0 if dtype == torch.bfloat16 else -20.0)
+        a[0, :64] = tiny * (1 + np.arange(64) % 4)
+        half_ulp[0, :64] = tiny / 2
+        P0 = torch.tensor(a, dtype=torch.float64).to(dtype)
+        P1 = torch.tensor(half_ulp, dtype=torch.float64).to(dtype)
+        assert torch.equal(P0.double(), torch.tensor(a)) and torch.equal(P1.double(),
+                                                                       torch.tensor(half_ulp))
+        R = torch.zeros(T, H, dtype=dtype)
+        w = torch.ones(H, dtype=dtype)
+        inp = {"partials": [P0.to(DEV), P1.to(DEV)], "residual": R.to(DEV), "weight": w.to(DEV)}
+        for flags in (arrms.FORCE_ROW, arrms.FORCE_SPLIT):
+            norm, res = run_rms(inp, 1e-6, False, flags=flags)
+            torch.cuda.synchronize()
+            check_rms(inp, norm, res, 1e-6, False, fmt=FMT[dtype])
+
+
+def test_special_values():
+    # eps = 0 on non-zero rows; an all-zero row with eps > 0; an inf in a row
+    # (that row's residual_out keeps the inf, its norm is NaN at the inf and 0
+    # elsewhere, exactly as the oracle's definition gives); large finite values
+    W, T, H = 2, 6, 512
+    inp = cuda_inputs(GENERIC, T, W=W, H=H, seed=99)
+    inp["partials"][0][1].zero_()
+    inp["partials"][1][1].zero_()
+    inp["residual"][1].zero_()
+    inp["partials"][0][2, 7] = float("inf")
+    inp["partials"][1][3] *= 1e15
+    for eps in (0.0, 1e-6):
+        if eps == 0.0:
+            sel = [0, 2, 3, 4, 5]      # the zero row has 0/0 with eps = 0
+        else:
+            sel = list(range(T))
+        norm, res = run_rms(inp, eps, False)
+        torch.cuda.synchronize()
+        check_rms(inp, norm, res, eps, False, rows=np.array(sel))
+
+
+def test_deterministic_and_row_split_agree():
+    wl = WORKLOADS["c2"]
+    inp = cuda_inputs(wl, 64)
+    a = run_rms(inp, wl.eps, True, flags=arrms.FORCE_ROW)
+    b = run_rms(inp, wl.eps, True, flags=arrms.FORCE_ROW)
+    s1 = run_rms(inp, wl.eps, True, flags=arrms.FORCE_SPLIT)
+    s2 = run_rms(inp, wl.eps, True, flags=arrms.FORCE_SPLIT)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(s1[0].view(torch.int16), s2[0].view(torch.int16))
+    assert torch.equal(a[1].view(torch.int16), s1[1].view(torch.int16))
+
+
+def test_graph_capture_replays_match_eager():
+    wl = WORKLOADS["c2"]
+    inp = cuda_inputs(wl, 8)
+    eager = run_rms(inp, wl.eps, True)
+    qinp = cuda_inputs(WORKLOADS["c4"], 32)
+    eager_q = arrms.fused_allreduce_rms_norm_quant(qinp["partials"], qinp["residual"],
+                                                   qinp["weight"], 1e-6, 128)
+    torch.cuda.synchronize()
+    plan = arrms.cached_plan(wl.W, 8, wl.H, arrms.BF16)
+    qplan = arrms.cached_plan(4, 32, 7168, arrms.BF16)
+    norm = torch.empty_like(eager[0])
+    res = torch.empty_like(eager[1])
+    qn, qq, qs, qr = (torch.empty_like(t) for t in eager_q)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps, True,
+                             norm, res, stream=s)
+            arrms.ar_rms_quant_run(qplan, qinp["partials"], qinp["residual"], qinp["weight"],
+                                   1e-6, False, 128, qn, qq, qs, qr, stream=s)
+    for _ in range(3):
+        norm.fill_(0)
+        qq.view(torch.uint8).fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(norm.view(torch.int16), eager[0].view(torch.int16))
+        assert torch.equal(res.view(torch.int16), eager[1].view(torch.int16))
+        assert torch.equal(qq.view(torch.uint8), eager_q[1].view(torch.uint8))
+        assert torch.equal(qs, eager_q[2])
+        _ = (inp["partials"][0].float() * 2).sum().item()   # eager work between replays
+
+
+def test_errors_leave_outputs_untouched():
+    x = torch.randn(8, 1024, device=DEV).to(torch.bfloat16)
+    w = torch.ones(1024, dtype=torch.bfloat16, device=DEV)
+    norm = torch.full_like(x, 7.0)
+    res = torch.full_like(x, 7.0)
+    plan = arrms.ar_rms_plan(2, 8, 1024)
+    buf = torch.empty(8 * 1024 + 8, dtype=torch.bfloat16, device=DEV)
+    misaligned = buf[1:1 + 8 * 1024].view(8, 1024)
+    with pytest.raises(arrms.ArrmsError) as e:
+        arrms.ar_rms_run(plan, [x, misaligned], x, w, 1e-6, False, norm, res)
+    assert e.value.code == arrms.EINVAL
+    with pytest.raises(arrms.ArrmsError) as e:
+        arrms.ar_rms_run(plan, [x, x], x, w, float("nan"), False, norm, res)
+    assert e.value.code == arrms.EINVAL
+    with pytest.raises(ValueError):
+        arrms.ar_rms_run(plan, [x, x[:4]], x, w, 1e-6, False, norm, res)
+    torch.cuda.synchronize()
+    assert bool((norm == 7.0).all()) and bool((res == 7.0).all())

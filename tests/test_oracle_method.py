@@ -130,7 +130,11 @@ def test_no_residual_equals_zero_residual():
     w = rand_bits(rng, (64,), 0.1, 1.0)
     a = oracle.ar_rms(P, None, w, 1e-6, False)
     b = oracle.ar_rms(P, np.zeros((3, 64), np.uint16), w, 1e-6, False)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2]) and a[1] is None
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+    # without a residual, residual_out is the rank-ordered fp32 sum alone
+    assert np.array_equal(val(a[1]), val(b[1]))
+    ref = torch.from_numpy(fp32_sum(P, None)).to(torch.bfloat16)
+    assert np.array_equal(a[1], ref.view(torch.int16).numpy().view(np.uint16))
 
 
 # ------------------------------------------------------------- closed forms

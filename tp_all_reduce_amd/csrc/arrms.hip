@@ -1,0 +1,648 @@
+// HIP kernels (gfx950, wave64) and the run entry points of libarrms.
+//
+// The fused tensor-parallel layer epilogue of the vLLM PR #54787 page
+// ("Motivation"; "Key source excerpts": fused_allreduce_gemma_rms_norm and
+// _rocm_aiter_fused_allreduce_rmsnorm_impl), on one GPU: W partial-sum
+// buffers [T, H] stand in for the W ranks' buffers and are reduced in the
+// kernel.  Per token row:
+//   phase 1  16-byte loads of all W partials and the residual, fp32 sum in
+//            rank order with the residual last, residual_out store, per-lane
+//            sum of squares;
+//   reduce   wave64 sum with DPP row ops plus readlane, one LDS exchange and
+//            one barrier across the workgroup's wavefronts;
+//   phase 2  rstd, (1 + w) or w, 16-bit norm_out store, and optionally the
+//            per-group FP8 epilogue (group amax by DPP within the lanes that
+//            hold the group, scale = amax / 448, E4M3FN codes).
+// The row stays in registers between the phases, so HBM sees each input once
+// and each output once: (W + 2) * T * H * 2 bytes plus the weight.
+//
+// Two launch shapes of the same kernel (chosen by the plan):
+//   row-resident  one workgroup per token row, one 16-byte pack per lane (up
+//                 to 1024 lanes = 8192 elements); lowest latency for the
+//                 decode window, where the launch and one DRAM round trip are
+//                 the whole cost;
+//   split         a persistent grid sized to what the CUs hold at once; each
+//                 workgroup loops over rows and issues the next row's loads
+//                 before it reduces and normalises the current one, so HBM
+//                 stays busy through the barrier and the epilogue.
+// Partials and residual are streamed with non-temporal loads (read once); the
+// weight row is loaded once per workgroup, after the first row's loads are in
+// flight, and kept in registers.
+//
+// There is no inter-workgroup communication, no atomics and no scratch
+// memory: every output is a fixed function of the inputs and bit-identical
+// from run to run.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "arrms_host.h"
+
+namespace arrms {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct Bf16 {};
+struct Fp16 {};
+
+// Two 16-bit elements per dword, element 0 in the low half.
+template <typename IO>
+struct Codec;
+
+template <>
+struct Codec<Bf16> {
+    static __device__ __forceinline__ f32x2 unpack(uint32_t u) {
+        return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+    }
+    // v_cvt_pk_bf16_f32: round to nearest even
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    }
+};
+
+template <>
+struct Codec<Fp16> {
+    static __device__ __forceinline__ f32x2 unpack(uint32_t u) {
+        return __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
+    }
+    // v_cvt_pk_f16_f32: round to nearest even
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+    }
+};
+
+template <typename IO>
+__device__ __forceinline__ void unpack8(u32x4 v, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x2 p = Codec<IO>::unpack(v[i]);
+        x[2 * i] = p.x;
+        x[2 * i + 1] = p.y;
+    }
+}
+
+template <typename IO>
+__device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = Codec<IO>::pack(x[2 * i], x[2 * i + 1]);
+    return v;
+}
+
+__device__ __forceinline__ u32x4 load16(const uint8_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Streaming load: the data is read exactly once.
+__device__ __forceinline__ u32x4 load16_stream(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ void store16(uint8_t *p, u32x4 v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// ---------------------------------------------------------------- wave64 ops
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // row_half_mirror: lane i <-> 7-i within 8 lanes
+constexpr int kRowMirror = 0x140;  // row_mirror: lane i <-> 15-i within 16 lanes
+
+// Sum over each 16-lane row; every lane of the row ends with the same bits
+// (each step adds a value to its mirror image, which is commutative).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<kQuadSwap1>(v);
+    v += dpp<kQuadSwap2>(v);
+    v += dpp<kHalfMirror>(v);
+    v += dpp<kRowMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Wave-uniform sum over all 64 lanes (all lanes must be active).
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// Max over aligned groups of `lanes` consecutive lanes (1..64, a power of two);
+// every lane of a group ends with the group's max.
+__device__ __forceinline__ float group_max(float v, int lanes) {
+    if (lanes >= 2) v = fmaxf(v, dpp<kQuadSwap1>(v));
+    if (lanes >= 4) v = fmaxf(v, dpp<kQuadSwap2>(v));
+    if (lanes >= 8) v = fmaxf(v, dpp<kHalfMirror>(v));
+    if (lanes >= 16) v = fmaxf(v, dpp<kRowMirror>(v));
+    if (lanes >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    if (lanes >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// fp32 -> OCP FP8 E4M3FN, round to nearest even, saturating at +-448, NaN to
+// 0x7F.  Normal range: keep 3 fraction bits of the fp32 pattern with
+// nearest-even rounding and re-bias the exponent from 127 to 7; below 2^-6 the
+// grid is the subnormal quantum 2^-9.
+__device__ __forceinline__ uint32_t to_e4m3(float v) {
+    if (v != v) return 0x7Fu;
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fminf(fabsf(v), 448.0f);
+    const uint32_t sub = uint32_t(__builtin_rintf(a * 512.0f));
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    const uint32_t nrm = (b >> 20) - (120u << 3);
+    return sign | (a < 0.015625f ? sub : nrm);
+}
+
+// ------------------------------------------------------- reduce + RMSNorm
+struct RmsParams {
+    const uint8_t *partials[kMaxW];
+    const uint8_t *residual;      // NULL: no residual term
+    const uint8_t *weight;
+    uint8_t *norm_out;            // NULL allowed in the quant variant
+    uint8_t *residual_out;        // NULL: dead residual output
+    uint8_t *q_out;               // quant variant: [T, H] codes
+    float *scales;                // quant variant: [T, H / group]
+    int64_t T;
+    int32_t H;
+    int32_t packs;                // H / 8
+    float eps;
+    int32_t gemma;                // weight applied as 1 + w (Gemma RMSNorm)
+    int32_t group_lanes;          // group_size / 8
+    int32_t groups;               // H / group_size
+};
+
+// Issues the loads of one row: W partial packs and the residual pack for each
+// of the lane's PPL packs (pack pk = lane + k * blockDim).
+template <int W, int PPL>
+__device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int tid, int nthr,
+                                         u32x4 (&v)[PPL][W + 1]) {
+    const size_t base = size_t(row) * size_t(p.H) * 2;
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+        const int pk = tid + k * nthr;
+        if (pk < p.packs) {
+            const size_t off = base + size_t(pk) * 16;
+#pragma unroll
+            for (int r = 0; r < W; ++r) v[k][r] = load16_stream(p.partials[r] + off);
+            v[k][W] = p.residual ? load16_stream(p.residual + off) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+// One pack per lane: up to 1024 lanes.  Several packs per lane (rows longer
+// than 1024 packs): up to 512 lanes, which leaves 256 registers per lane.
+constexpr int rms_block_bound(int ppl) { return ppl == 1 ? kMaxBlock : kMaxBlock / 2; }
+
+template <typename IO, int W, int PPL, bool PREFETCH, bool QUANT>
+__global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsParams p) {
+    __shared__ float wave_sums[2][kMaxBlock / 64];
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int nwaves = nthr >> 6;
+    const int64_t stride = gridDim.x;
+    int64_t row = blockIdx.x;
+    if (row >= p.T) return;      // the whole workgroup leaves together
+
+    u32x4 in[PPL][W + 1];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k)
+#pragma unroll
+        for (int r = 0; r <= W; ++r) in[k][r] = u32x4{0u, 0u, 0u, 0u};
+    load_row<W, PPL>(p, row, tid, nthr, in);
+    // weight row: issued after the first row's loads, kept for every row
+    u32x4 wraw[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+        const int pk = tid + k * nthr;
+        wraw[k] = pk < p.packs ? load16(p.weight + size_t(pk) * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    int parity = 0;
+    for (;;) {
+        u32x4 cur[PPL][W + 1];
+#pragma unroll
+        for (int k = 0; k < PPL; ++k)
+#pragma unroll
+            for (int r = 0; r <= W; ++r) cur[k][r] = in[k][r];
+        const int64_t next = row + stride;
+        if constexpr (PREFETCH) {
+            if (next < p.T) load_row<W, PPL>(p, next, tid, nthr, in);
+        }
+        const size_t base = size_t(row) * size_t(p.H) * 2;
+
+        // phase 1: rank-ordered fp32 sum, residual last, residual_out
+        float acc[PPL][8];
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int pk = tid + k * nthr;
+            unpack8<IO>(cur[k][0], acc[k]);
+#pragma unroll
+            for (int r = 1; r < W; ++r) {
+                float x[8];
+                unpack8<IO>(cur[k][r], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[k][i] = acc[k][i] + x[i];
+            }
+            if (p.residual) {
+                float x[8];
+                unpack8<IO>(cur[k][W], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[k][i] = acc[k][i] + x[i];
+            }
+            if (pk < p.packs) {
+                if (p.residual_out) store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[k][i] = 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(acc[k][i], acc[k][i], ss);
+        }
+
+        // sum of squares over the row: wave64 reduce, then across wavefronts
+        const float wsum = wave_sum(ss);
+        if ((tid & 63) == 0) wave_sums[parity][tid >> 6] = wsum;
+        __syncthreads();
+        float total = 0.0f;
+        for (int i = 0; i < nwaves; ++i) total += wave_sums[parity][i];
+        const float rstd = rsqrtf(total / float(p.H) + p.eps);
+
+        // phase 2: normalise, weight, store; optional FP8 group epilogue
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int pk = tid + k * nthr;
+            const bool valid = pk < p.packs;
+            float w[8];
+            unpack8<IO>(wraw[k], w);
+            if (p.gemma) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[i] = w[i] + 1.0f;
+            }
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = (acc[k][i] * rstd) * w[i];
+            if (valid && p.norm_out)
+                store16(p.norm_out + base + size_t(pk) * 16, pack8<IO>(y));
+            if constexpr (QUANT) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+                amax = group_max(amax, p.group_lanes);
+                const float scale = amax / 448.0f;
+                uint32_t lo = 0, hi = 0;
+                if (scale != 0.0f) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) lo |= to_e4m3(y[i] / scale) << (8 * i);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hi |= to_e4m3(y[4 + i] / scale) << (8 * i);
+                }
+                if (valid) {
+                    *reinterpret_cast<u32x2 *>(p.q_out + size_t(row) * p.H + size_t(pk) * 8) =
+                        u32x2{lo, hi};
+                    if ((pk & (p.group_lanes - 1)) == 0)
+                        p.scales[size_t(row) * p.groups + pk / p.group_lanes] = scale;
+                }
+            }
+        }
+
+        if (next >= p.T) break;
+        row = next;
+        parity ^= 1;
+        if constexpr (!PREFETCH) load_row<W, PPL>(p, row, tid, nthr, in);
+    }
+}
+
+// ------------------------------------------------------------- QK-norm
+struct QkParams {
+    const uint8_t *qkv[kMaxW];
+    const uint8_t *q_weight;
+    const uint8_t *k_weight;
+    uint8_t *q_out;
+    uint8_t *k_out;
+    int64_t T;
+    int32_t W;
+    int32_t q_packs;              // q_size / 8
+    int32_t kv_packs;             // kv_size / 8
+    int32_t row_bytes;            // (q_size + 2 kv_size) * 2
+    float eps;
+};
+
+// One workgroup per token.  Lanes cover the W shards' q packs first, then
+// their k packs; each lane adds its squares to the q or the k statistic, and
+// both statistics are reduced across the workgroup together.  Lane pack idx
+// of shard r reads global weight column r * size + j, which is pack idx of
+// the concatenated weight.
+template <typename IO, int PPL>
+__global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(QkParams p) {
+    __shared__ float wave_sums[2][2][kMaxBlock / 64];
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int nwaves = nthr >> 6;
+    const int nq = p.W * p.q_packs;
+    const int n = nq + p.W * p.kv_packs;
+    const int q_size = p.q_packs * 8;
+    const int kv_size = p.kv_packs * 8;
+
+    int parity = 0;
+    for (int64_t row = blockIdx.x; row < p.T; row += gridDim.x, parity ^= 1) {
+        u32x4 xr[PPL], wr[PPL];
+        // loads first (activations, then weights), arithmetic after
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int pk = tid + k * nthr;
+            xr[k] = u32x4{0u, 0u, 0u, 0u};
+            wr[k] = u32x4{0u, 0u, 0u, 0u};
+            if (pk < n) {
+                const bool is_q = pk < nq;
+                const int idx = is_q ? pk : pk - nq;
+                const int per = is_q ? p.q_packs : p.kv_packs;
+                const int r = idx / per;
+                const int j = idx - r * per + (is_q ? 0 : p.q_packs);
+                xr[k] = load16_stream(p.qkv[r] + size_t(row) * p.row_bytes + size_t(j) * 16);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int pk = tid + k * nthr;
+            if (pk < n) {
+                const bool is_q = pk < nq;
+                const int idx = is_q ? pk : pk - nq;
+                wr[k] = load16((is_q ? p.q_weight : p.k_weight) + size_t(idx) * 16);
+            }
+        }
+        float x[PPL][8];
+        float ssq = 0.0f, ssk = 0.0f;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int pk = tid + k * nthr;
+            unpack8<IO>(xr[k], x[k]);
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s = __builtin_fmaf(x[k][i], x[k][i], s);
+            if (pk < nq) ssq += s; else ssk += s;
+        }
+        const float wq = wave_sum(ssq);
+        const float wk = wave_sum(ssk);
+        if ((tid & 63) == 0) {
+            wave_sums[parity][0][tid >> 6] = wq;
+            wave_sums[parity][1][tid >> 6] = wk;
+        }
+        __syncthreads();
+        float tq = 0.0f, tk = 0.0f;
+        for (int i = 0; i < nwaves; ++i) {
+            tq += wave_sums[parity][0][i];
+            tk += wave_sums[parity][1][i];
+        }
+        const float rq = rsqrtf(tq / float(p.W * q_size) + p.eps);
+        const float rk = rsqrtf(tk / float(p.W * kv_size) + p.eps);
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int pk = tid + k * nthr;
+            if (pk < n) {
+                const bool is_q = pk < nq;
+                const int idx = is_q ? pk : pk - nq;
+                const int per = is_q ? p.q_packs : p.kv_packs;
+                const int r = idx / per;
+                const int j = idx - r * per;
+                float wv[8];
+                unpack8<IO>(wr[k], wv);
+                const float rs = is_q ? rq : rk;
+                float y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = (x[k][i] * rs) * wv[i];
+                uint8_t *out = is_q ? p.q_out + ((size_t(r) * p.T + row) * q_size) * 2
+                                    : p.k_out + ((size_t(r) * p.T + row) * kv_size) * 2;
+                store16(out + size_t(j) * 16, pack8<IO>(y));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- launchers
+using RmsLaunch = hipError_t (*)(const RmsParams &, unsigned, unsigned, hipStream_t);
+using QkLaunch = hipError_t (*)(const QkParams &, unsigned, unsigned, hipStream_t);
+
+template <typename IO, int W, int PPL, bool PREFETCH, bool QUANT>
+hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStream_t s) {
+    RmsParams local = p;
+    void *args[] = {&local};
+    return hipLaunchKernel(
+        reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, PREFETCH, QUANT>),
+        dim3(grid), dim3(block), args, 0, s);
+}
+
+template <typename IO, int PPL>
+hipError_t launch_qk(const QkParams &p, unsigned grid, unsigned block, hipStream_t s) {
+    QkParams local = p;
+    void *args[] = {&local};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&qknorm_kernel<IO, PPL>), dim3(grid),
+                           dim3(block), args, 0, s);
+}
+
+template <typename IO, int W, bool QUANT>
+const void *rms_symbol(int ppl, bool prefetch) {
+    if (ppl == 1)
+        return prefetch ? reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, 1, true, QUANT>)
+                        : reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, 1, false, QUANT>);
+    return reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, 4, false, QUANT>);
+}
+
+template <typename IO, int W, bool QUANT>
+RmsLaunch pick_variant(int ppl, bool prefetch) {
+    if (ppl == 1) return prefetch ? &launch_rms<IO, W, 1, true, QUANT> : &launch_rms<IO, W, 1, false, QUANT>;
+    if (ppl == 4 && !prefetch) return &launch_rms<IO, W, 4, false, QUANT>;
+    return nullptr;
+}
+
+template <typename IO, bool QUANT>
+RmsLaunch pick_w(int W, int ppl, bool prefetch) {
+    switch (W) {
+    case 1: return pick_variant<IO, 1, QUANT>(ppl, prefetch);
+    case 2: return pick_variant<IO, 2, QUANT>(ppl, prefetch);
+    case 3: return pick_variant<IO, 3, QUANT>(ppl, prefetch);
+    case 4: return pick_variant<IO, 4, QUANT>(ppl, prefetch);
+    case 5: return pick_variant<IO, 5, QUANT>(ppl, prefetch);
+    case 6: return pick_variant<IO, 6, QUANT>(ppl, prefetch);
+    case 7: return pick_variant<IO, 7, QUANT>(ppl, prefetch);
+    case 8: return pick_variant<IO, 8, QUANT>(ppl, prefetch);
+    default: return nullptr;
+    }
+}
+
+template <typename IO, bool QUANT>
+const void *symbol_w(int W, int ppl, bool prefetch) {
+    switch (W) {
+    case 1: return rms_symbol<IO, 1, QUANT>(ppl, prefetch);
+    case 2: return rms_symbol<IO, 2, QUANT>(ppl, prefetch);
+    case 3: return rms_symbol<IO, 3, QUANT>(ppl, prefetch);
+    case 4: return rms_symbol<IO, 4, QUANT>(ppl, prefetch);
+    case 5: return rms_symbol<IO, 5, QUANT>(ppl, prefetch);
+    case 6: return rms_symbol<IO, 6, QUANT>(ppl, prefetch);
+    case 7: return rms_symbol<IO, 7, QUANT>(ppl, prefetch);
+    case 8: return rms_symbol<IO, 8, QUANT>(ppl, prefetch);
+    default: return nullptr;
+    }
+}
+
+struct Variant {
+    RmsLaunch launch;
+    const void *symbol;
+};
+
+Variant pick_rms(int dtype, int W, int ppl, bool prefetch, bool quant) {
+    if (dtype == ARRMS_BF16)
+        return quant ? Variant{pick_w<Bf16, true>(W, ppl, prefetch), symbol_w<Bf16, true>(W, ppl, prefetch)}
+                     : Variant{pick_w<Bf16, false>(W, ppl, prefetch), symbol_w<Bf16, false>(W, ppl, prefetch)};
+    return quant ? Variant{pick_w<Fp16, true>(W, ppl, prefetch), symbol_w<Fp16, true>(W, ppl, prefetch)}
+                 : Variant{pick_w<Fp16, false>(W, ppl, prefetch), symbol_w<Fp16, false>(W, ppl, prefetch)};
+}
+
+template <typename IO>
+QkLaunch pick_qk_ppl(int ppl) {
+    switch (ppl) {
+    case 1: return &launch_qk<IO, 1>;
+    case 2: return &launch_qk<IO, 2>;
+    case 4: return &launch_qk<IO, 4>;
+    default: return nullptr;
+    }
+}
+
+// Workgroups of the split kernel that the device holds at once (CUs times
+// resident workgroups per CU for this kernel and block size); the persistent
+// grid is min(T, this).  Queried once per (device, kernel, block) and cached.
+int resident_grid(const void *symbol, int block) {
+    struct Entry {
+        int device;
+        const void *symbol;
+        int block;
+        int grid;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : cache)
+            if (e.device == dev && e.symbol == symbol && e.block == block) return e.grid;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, symbol, block, 0) != hipSuccess)
+        return -1;
+    const int grid = cus * (per_cu > 0 ? per_cu : 1);
+    std::lock_guard<std::mutex> lock(mu);
+    cache.push_back(Entry{dev, symbol, block, grid});
+    return grid;
+}
+
+int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *residual,
+            const void *weight, float eps, int gemma, void *norm_out, void *residual_out,
+            bool quant, int group_size, uint8_t *q_out, float *scales, void *stream) {
+    if (plan->T == 0) return ARRMS_OK;
+    RmsParams p{};
+    for (int r = 0; r < plan->W; ++r) p.partials[r] = static_cast<const uint8_t *>(partials[r]);
+    p.residual = static_cast<const uint8_t *>(residual);
+    p.weight = static_cast<const uint8_t *>(weight);
+    p.norm_out = static_cast<uint8_t *>(norm_out);
+    p.residual_out = static_cast<uint8_t *>(residual_out);
+    p.q_out = q_out;
+    p.scales = scales;
+    p.T = plan->T;
+    p.H = int32_t(plan->H);
+    p.packs = int32_t(plan->H / kPackElems);
+    p.eps = eps;
+    p.gemma = gemma ? 1 : 0;
+    p.group_lanes = quant ? group_size / kPackElems : 1;
+    p.groups = quant ? int32_t(plan->H / group_size) : 0;
+    const bool split = plan->kernel == ARRMS_KERNEL_SPLIT;
+    const bool prefetch = split && plan->ppl == 1;
+    Variant v = pick_rms(plan->dtype, plan->W, plan->ppl, prefetch, quant);
+    if (v.launch == nullptr)
+        return fail(ARRMS_ENOTSUP, "no kernel for W=%d, %d packs per lane", plan->W, plan->ppl);
+    int64_t grid = plan->T;
+    if (split) {
+        const int resident = resident_grid(v.symbol, plan->block);
+        if (resident <= 0) return fail(ARRMS_EHIP, "device occupancy query failed");
+        if (grid > resident) grid = resident;
+    }
+    hipError_t e = v.launch(p, unsigned(grid), unsigned(plan->block), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(ARRMS_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ARRMS_OK;
+}
+
+}  // namespace
+}  // namespace arrms
+
+using namespace arrms;
+
+extern "C" int ar_rms_run(const ar_rms_plan_s *plan, const void *const *partials,
+                          const void *residual, const void *weight, float eps, int gemma,
+                          void *norm_out, void *residual_out, void *stream) {
+    clear_error();
+    int rc = check_rms_args(plan, partials, residual, weight, eps, norm_out, true, residual_out);
+    if (rc) return rc;
+    return run_rms(plan, partials, residual, weight, eps, gemma, norm_out, residual_out, false, 0,
+                   nullptr, nullptr, stream);
+}
+
+extern "C" int ar_rms_quant_run(const ar_rms_plan_s *plan, const void *const *partials,
+                                const void *residual, const void *weight, float eps, int gemma,
+                                int group_size, void *norm_out, uint8_t *q_out, float *scales,
+                                void *residual_out, void *stream) {
+    clear_error();
+    int rc = check_rms_args(plan, partials, residual, weight, eps, norm_out, false, residual_out);
+    if (rc) return rc;
+    rc = check_quant_args(plan, group_size, q_out, scales);
+    if (rc) return rc;
+    return run_rms(plan, partials, residual, weight, eps, gemma, norm_out, residual_out, true,
+                   group_size, q_out, scales, stream);
+}
+
+extern "C" int ar_qknorm_run(const ar_rms_plan_s *plan, const void *const *qkv, int q_size,
+                             int kv_size, const void *q_weight, const void *k_weight, float eps,
+                             void *q_out, void *k_out, void *stream) {
+    clear_error();
+    int rc = check_qk_args(plan, qkv, q_size, kv_size, q_weight, k_weight, eps, q_out, k_out);
+    if (rc) return rc;
+    if (plan->T == 0) return ARRMS_OK;
+    QkParams p{};
+    for (int r = 0; r < plan->W; ++r) p.qkv[r] = static_cast<const uint8_t *>(qkv[r]);
+    p.q_weight = static_cast<const uint8_t *>(q_weight);
+    p.k_weight = static_cast<const uint8_t *>(k_weight);
+    p.q_out = static_cast<uint8_t *>(q_out);
+    p.k_out = static_cast<uint8_t *>(k_out);
+    p.T = plan->T;
+    p.W = plan->W;
+    p.q_packs = q_size / kPackElems;
+    p.kv_packs = kv_size / kPackElems;
+    p.row_bytes = int32_t(plan->H * 2);
+    p.eps = eps;
+    Shape s = qk_shape(plan->W, q_size, kv_size);
+    QkLaunch fn = plan->dtype == ARRMS_BF16 ? pick_qk_ppl<Bf16>(s.ppl) : pick_qk_ppl<Fp16>(s.ppl);
+    if (fn == nullptr) return fail(ARRMS_ENOTSUP, "no QK kernel for %d packs per lane", s.ppl);
+    // one workgroup per token; beyond 65536 tokens workgroups loop over tokens
+    const int64_t grid = plan->T < 65536 ? plan->T : 65536;
+    hipError_t e = fn(p, unsigned(grid), unsigned(s.block), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(ARRMS_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ARRMS_OK;
+}
