@@ -186,11 +186,11 @@ struct RmsParams {
     int32_t groups;               // H / group_size
 };
 
-// Issues the loads of one row: W partial packs and the residual pack for each
-// of the lane's PPL packs (pack pk = lane + k * blockDim).
-template <int W, int PPL>
+// Issues the loads of one row: W partial packs and (RES) the residual pack for
+// each of the lane's PPL packs (pack pk = lane + k * blockDim).
+template <int W, int PPL, bool RES>
 __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int tid, int nthr,
-                                         u32x4 (&v)[PPL][W + 1]) {
+                                         u32x4 (&v)[PPL][W + RES]) {
     const size_t base = size_t(row) * size_t(p.H) * 2;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
@@ -199,7 +199,7 @@ __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int ti
             const size_t off = base + size_t(pk) * 16;
 #pragma unroll
             for (int r = 0; r < W; ++r) v[k][r] = load16_stream(p.partials[r] + off);
-            v[k][W] = p.residual ? load16_stream(p.residual + off) : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (RES) v[k][W] = load16_stream(p.residual + off);
         }
     }
 }
@@ -208,40 +208,63 @@ __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int ti
 // than 1024 packs): up to 512 lanes, which leaves 256 registers per lane.
 constexpr int rms_block_bound(int ppl) { return ppl == 1 ? kMaxBlock : kMaxBlock / 2; }
 
-template <typename IO, int W, int PPL, bool PREFETCH, bool QUANT>
+// Kernel modes.  kRow: one row per workgroup, straight-line code.  kSplit:
+// persistent workgroups looping over rows, the next row's loads issued one row
+// ahead.  kSplitWide: persistent, several packs per lane, loads at the top of
+// each row (no room in registers for a second row).
+enum Mode { kRow = 0, kSplit = 1, kSplitWide = 2 };
+
+// RES: a residual term is present (compile-time, so that every load of a row
+// is issued before the first wait).
+template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
 __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsParams p) {
     __shared__ float wave_sums[2][kMaxBlock / 64];
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
     const int nwaves = nthr >> 6;
     const int64_t stride = gridDim.x;
-    int64_t row = blockIdx.x;
-    if (row >= p.T) return;      // the whole workgroup leaves together
+    int64_t row = blockIdx.x;    // < T: the launcher never starts more workgroups than rows
 
-    u32x4 in[PPL][W + 1];
-#pragma unroll
-    for (int k = 0; k < PPL; ++k)
-#pragma unroll
-        for (int r = 0; r <= W; ++r) in[k][r] = u32x4{0u, 0u, 0u, 0u};
-    load_row<W, PPL>(p, row, tid, nthr, in);
-    // weight row: issued after the first row's loads, kept for every row
-    u32x4 wraw[PPL];
-#pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-        const int pk = tid + k * nthr;
-        wraw[k] = pk < p.packs ? load16(p.weight + size_t(pk) * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
-
-    int parity = 0;
-    for (;;) {
-        u32x4 cur[PPL][W + 1];
+    constexpr int NB = W + RES;      // packs loaded per lane pack: partials, residual
+    // kSplit: `ahead` receives the next row's loads one row in advance
+    u32x4 ahead[PPL][NB];
+    if constexpr (MODE == kSplit) {
 #pragma unroll
         for (int k = 0; k < PPL; ++k)
 #pragma unroll
-            for (int r = 0; r <= W; ++r) cur[k][r] = in[k][r];
+            for (int r = 0; r < NB; ++r) ahead[k][r] = u32x4{0u, 0u, 0u, 0u};
+        load_row<W, PPL, RES>(p, row, tid, nthr, ahead);
+    }
+    // weight row: loaded once per workgroup and kept (kSplitWide reloads it
+    // per row from L2 to stay within registers); converted where used, so no
+    // wait on it stands before the row's loads
+    u32x4 wraw[PPL];
+    auto load_weight = [&]() {
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int pk = tid + k * nthr;
+            wraw[k] = pk < p.packs ? load16(p.weight + size_t(pk) * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    if constexpr (MODE != kSplitWide) load_weight();
+
+    int parity = 0;
+    for (;;) {
+        u32x4 cur[PPL][NB];
         const int64_t next = row + stride;
-        if constexpr (PREFETCH) {
-            if (next < p.T) load_row<W, PPL>(p, next, tid, nthr, in);
+        if constexpr (MODE == kSplit) {
+#pragma unroll
+            for (int k = 0; k < PPL; ++k)
+#pragma unroll
+                for (int r = 0; r < NB; ++r) cur[k][r] = ahead[k][r];
+            if (next < p.T) load_row<W, PPL, RES>(p, next, tid, nthr, ahead);
+        } else {
+#pragma unroll
+            for (int k = 0; k < PPL; ++k)
+#pragma unroll
+                for (int r = 0; r < NB; ++r) cur[k][r] = u32x4{0u, 0u, 0u, 0u};
+            load_row<W, PPL, RES>(p, row, tid, nthr, cur);
+            if constexpr (MODE == kSplitWide) load_weight();
         }
         const size_t base = size_t(row) * size_t(p.H) * 2;
 
@@ -259,7 +282,7 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsPa
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[k][i] = acc[k][i] + x[i];
             }
-            if (p.residual) {
+            if constexpr (RES) {
                 float x[8];
                 unpack8<IO>(cur[k][W], x);
 #pragma unroll
@@ -321,10 +344,9 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsPa
             }
         }
 
-        if (next >= p.T) break;
+        if (MODE == kRow || next >= p.T) break;
         row = next;
         parity ^= 1;
-        if constexpr (!PREFETCH) load_row<W, PPL>(p, row, tid, nthr, in);
     }
 }
 
@@ -438,12 +460,12 @@ __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(QkParams p) {
 using RmsLaunch = hipError_t (*)(const RmsParams &, unsigned, unsigned, hipStream_t);
 using QkLaunch = hipError_t (*)(const QkParams &, unsigned, unsigned, hipStream_t);
 
-template <typename IO, int W, int PPL, bool PREFETCH, bool QUANT>
+template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
 hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStream_t s) {
     RmsParams local = p;
     void *args[] = {&local};
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, PREFETCH, QUANT>),
+        reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES>),
         dim3(grid), dim3(block), args, 0, s);
 }
 
@@ -455,62 +477,54 @@ hipError_t launch_qk(const QkParams &p, unsigned grid, unsigned block, hipStream
                            dim3(block), args, 0, s);
 }
 
-template <typename IO, int W, bool QUANT>
-const void *rms_symbol(int ppl, bool prefetch) {
-    if (ppl == 1)
-        return prefetch ? reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, 1, true, QUANT>)
-                        : reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, 1, false, QUANT>);
-    return reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, 4, false, QUANT>);
-}
-
-template <typename IO, int W, bool QUANT>
-RmsLaunch pick_variant(int ppl, bool prefetch) {
-    if (ppl == 1) return prefetch ? &launch_rms<IO, W, 1, true, QUANT> : &launch_rms<IO, W, 1, false, QUANT>;
-    if (ppl == 4 && !prefetch) return &launch_rms<IO, W, 4, false, QUANT>;
-    return nullptr;
-}
-
-template <typename IO, bool QUANT>
-RmsLaunch pick_w(int W, int ppl, bool prefetch) {
-    switch (W) {
-    case 1: return pick_variant<IO, 1, QUANT>(ppl, prefetch);
-    case 2: return pick_variant<IO, 2, QUANT>(ppl, prefetch);
-    case 3: return pick_variant<IO, 3, QUANT>(ppl, prefetch);
-    case 4: return pick_variant<IO, 4, QUANT>(ppl, prefetch);
-    case 5: return pick_variant<IO, 5, QUANT>(ppl, prefetch);
-    case 6: return pick_variant<IO, 6, QUANT>(ppl, prefetch);
-    case 7: return pick_variant<IO, 7, QUANT>(ppl, prefetch);
-    case 8: return pick_variant<IO, 8, QUANT>(ppl, prefetch);
-    default: return nullptr;
-    }
-}
-
-template <typename IO, bool QUANT>
-const void *symbol_w(int W, int ppl, bool prefetch) {
-    switch (W) {
-    case 1: return rms_symbol<IO, 1, QUANT>(ppl, prefetch);
-    case 2: return rms_symbol<IO, 2, QUANT>(ppl, prefetch);
-    case 3: return rms_symbol<IO, 3, QUANT>(ppl, prefetch);
-    case 4: return rms_symbol<IO, 4, QUANT>(ppl, prefetch);
-    case 5: return rms_symbol<IO, 5, QUANT>(ppl, prefetch);
-    case 6: return rms_symbol<IO, 6, QUANT>(ppl, prefetch);
-    case 7: return rms_symbol<IO, 7, QUANT>(ppl, prefetch);
-    case 8: return rms_symbol<IO, 8, QUANT>(ppl, prefetch);
-    default: return nullptr;
-    }
-}
-
+// A kernel variant: its launcher and its symbol (for the occupancy query).
 struct Variant {
     RmsLaunch launch;
     const void *symbol;
 };
 
-Variant pick_rms(int dtype, int W, int ppl, bool prefetch, bool quant) {
-    if (dtype == ARRMS_BF16)
-        return quant ? Variant{pick_w<Bf16, true>(W, ppl, prefetch), symbol_w<Bf16, true>(W, ppl, prefetch)}
-                     : Variant{pick_w<Bf16, false>(W, ppl, prefetch), symbol_w<Bf16, false>(W, ppl, prefetch)};
-    return quant ? Variant{pick_w<Fp16, true>(W, ppl, prefetch), symbol_w<Fp16, true>(W, ppl, prefetch)}
-                 : Variant{pick_w<Fp16, false>(W, ppl, prefetch), symbol_w<Fp16, false>(W, ppl, prefetch)};
+template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
+Variant variant() {
+    return Variant{&launch_rms<IO, W, PPL, MODE, QUANT, RES>,
+                   reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES>)};
+}
+
+// Modes built: kRow and kSplit with one pack per lane, kSplitWide with four
+// packs per lane (rows longer than 8192 elements).
+template <typename IO, int W, bool QUANT, bool RES>
+Variant pick_mode(int mode) {
+    switch (mode) {
+    case kRow: return variant<IO, W, 1, kRow, QUANT, RES>();
+    case kSplit: return variant<IO, W, 1, kSplit, QUANT, RES>();
+    case kSplitWide: return variant<IO, W, kMaxPpl, kSplitWide, QUANT, RES>();
+    default: return Variant{nullptr, nullptr};
+    }
+}
+
+template <typename IO, bool QUANT, bool RES>
+Variant pick_w(int W, int mode) {
+    switch (W) {
+    case 1: return pick_mode<IO, 1, QUANT, RES>(mode);
+    case 2: return pick_mode<IO, 2, QUANT, RES>(mode);
+    case 3: return pick_mode<IO, 3, QUANT, RES>(mode);
+    case 4: return pick_mode<IO, 4, QUANT, RES>(mode);
+    case 5: return pick_mode<IO, 5, QUANT, RES>(mode);
+    case 6: return pick_mode<IO, 6, QUANT, RES>(mode);
+    case 7: return pick_mode<IO, 7, QUANT, RES>(mode);
+    case 8: return pick_mode<IO, 8, QUANT, RES>(mode);
+    default: return Variant{nullptr, nullptr};
+    }
+}
+
+template <typename IO>
+Variant pick_io(int W, int mode, bool quant, bool res) {
+    if (quant) return res ? pick_w<IO, true, true>(W, mode) : pick_w<IO, true, false>(W, mode);
+    return res ? pick_w<IO, false, true>(W, mode) : pick_w<IO, false, false>(W, mode);
+}
+
+Variant pick_rms(int dtype, int W, int mode, bool quant, bool res) {
+    return dtype == ARRMS_BF16 ? pick_io<Bf16>(W, mode, quant, res)
+                               : pick_io<Fp16>(W, mode, quant, res);
 }
 
 template <typename IO>
@@ -573,8 +587,8 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
     p.group_lanes = quant ? group_size / kPackElems : 1;
     p.groups = quant ? int32_t(plan->H / group_size) : 0;
     const bool split = plan->kernel == ARRMS_KERNEL_SPLIT;
-    const bool prefetch = split && plan->ppl == 1;
-    Variant v = pick_rms(plan->dtype, plan->W, plan->ppl, prefetch, quant);
+    const int mode = !split ? kRow : (plan->ppl == 1 ? kSplit : kSplitWide);
+    Variant v = pick_rms(plan->dtype, plan->W, mode, quant, residual != nullptr);
     if (v.launch == nullptr)
         return fail(ARRMS_ENOTSUP, "no kernel for W=%d, %d packs per lane", plan->W, plan->ppl);
     int64_t grid = plan->T;
