@@ -10,8 +10,9 @@ calls, one per T, replayed from a HIP graph; inputs are resident in HBM before
 the timed region starts.  value = microseconds per fused call (step time / 10).
 
 The roofline object covers the dominant kernel (the row-resident kernel, every
-launch of the step): algorithmic bytes per launch, (W + 2) * T * H * 2 + H * 2
-averaged over the sweep, divided by that kernel's average launch duration,
+launch of the step): algorithmic bytes per launch, (W + 3) * T * H * 2 + H * 2
+(W partials and the residual read, norm_out and residual_out written, the
+weight read once) averaged over the sweep, divided by that kernel's average launch duration,
 measured with HIP events on the stream the graph is replayed on.  `traffic` is
 read from the committed rocprofv3 counter summary when it was taken on the
 current kernel source, else null.
@@ -42,6 +43,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_kernel_c2_sweep.json"
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def rms_bytes(W, T, H, group=0, residual=True):
+    """Algorithmic HBM bytes of one fused call on 16-bit data: W partials and
+    the residual read, residual_out and norm_out written, the weight read once;
+    with the FP8 epilogue also the codes (1 byte per element) and the fp32
+    group scales."""
+    n = (W + (1 if residual else 0) + 2) * T * H * 2 + H * 2
+    if group:
+        n += T * H + 4 * T * (H // group)
+    return n
 
 
 def kernel_source_sha() -> str:
@@ -144,7 +156,7 @@ def main():
     us_per_call, ms_total = graph_time(torch, step, args.steps, args.warmup, len(Ts), stream)
     ms_per_step = ms_total / args.steps
     H, W = wl.H, wl.W
-    bytes_per_launch = sum((W + 2) * T * H * 2 + H * 2 for T in Ts) / len(Ts)
+    bytes_per_launch = sum(rms_bytes(W, T, H) for T in Ts) / len(Ts)
     achieved = bytes_per_launch / (us_per_call * 1e-6) / 1e9
     log(f"[bench] {us_per_call:.3f} us/call (graph), {achieved:.1f} GB/s algorithmic")
 
@@ -266,7 +278,7 @@ def full_report(torch, arrms, workloads, WORKLOADS, dev, stream, args):
                     wl.W * (wl.q_size + wl.kv_size) * 2
                 reps, n_calls = 50, 20
             else:
-                big = T * wl.H * (wl.W + 2) * 2 > (1 << 29)
+                big = rms_bytes(wl.W, T, wl.H) > (1 << 29)
                 sets = 1 if big else 3
                 inps = []
                 for s in range(sets):
@@ -293,9 +305,7 @@ def full_report(torch, arrms, workloads, WORKLOADS, dev, stream, args):
                             arrms.ar_rms_run(plan, inp["partials"], inp["residual"],
                                              inp["weight"], wl.eps, wl.gemma, norm, res,
                                              stream=stream)
-                nbytes = (wl.W + 2) * T * wl.H * 2 + wl.H * 2
-                if quant:
-                    nbytes += T * wl.H + 4 * T * (wl.H // wl.group)
+                nbytes = rms_bytes(wl.W, T, wl.H, wl.group)
                 reps = 10 if big else 50
             us, _ = graph_time(torch, call, reps, 2, n_calls, stream)
             gbs = nbytes / (us * 1e-6) / 1e9
