@@ -6,8 +6,11 @@
 Workload of the headline line: the decode-window sweep, W=4 partial buffers of
 [T, 4096] bf16 with Gemma RMSNorm, eps 1e-6, T in {1, 2, 4, 8, 16, 21, 22, 32,
 64, 80}, row-resident kernel.  One step is one pass over the sweep: ten fused
-calls, one per T, replayed from a HIP graph; inputs are resident in HBM before
-the timed region starts.  value = microseconds per fused call (step time / 10).
+calls, one per T; inputs are resident in HBM before the timed region starts.
+Steps are launched from a HIP graph that holds --steps-per-graph of them (as a
+captured decode step holds every layer's epilogue); the K timed steps are K /
+steps-per-graph replays.  value = microseconds per fused call (step time / 10).
+The config also reports the figure with one step per graph.
 
 The roofline object covers the dominant kernel (the row-resident kernel, every
 launch of the step): algorithmic bytes per launch, (W + 3) * T * H * 2 + H * 2
@@ -65,7 +68,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps-per-graph", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-large-t", action="store_true",
+                    help="skip the W=8 [8192, 8192] prefill figure reported beside the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--full", default=None,
                     help="also time every workload (c1..c5) and write a JSON report here")
@@ -152,9 +158,21 @@ def main():
             arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
                              True, norm, res, stream=stream)
 
-    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps")
-    us_per_call, ms_total = graph_time(torch, step, args.steps, args.warmup, len(Ts), stream)
+    spg = max(1, args.steps_per_graph)
+    if args.steps % spg or args.warmup % spg:
+        sys.exit(f"--steps and --warmup must be multiples of --steps-per-graph ({spg})")
+
+    def steps():
+        for _ in range(spg):
+            step()
+
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps "
+        f"({spg} steps per graph replay)")
+    us_per_call, ms_total = graph_time(torch, steps, args.steps // spg, args.warmup // spg,
+                                       len(Ts) * spg, stream)
     ms_per_step = ms_total / args.steps
+    us_one_step_graph, _ = graph_time(torch, step, 500, 20, len(Ts), stream)
+    log(f"[bench] one step per graph replay: {us_one_step_graph:.3f} us/call")
     H, W = wl.H, wl.W
     bytes_per_launch = sum(rms_bytes(W, T, H) for T in Ts) / len(Ts)
     achieved = bytes_per_launch / (us_per_call * 1e-6) / 1e9
@@ -167,10 +185,10 @@ def main():
 
         def one(case=case):
             T_, inp_, plan_, norm_, res_ = case
-            for _ in range(20):
+            for _ in range(len(Ts) * spg):
                 arrms.ar_rms_run(plan_, inp_["partials"], inp_["residual"], inp_["weight"],
                                  wl.eps, True, norm_, res_, stream=stream)
-        us, _ = graph_time(torch, one, 50, 5, 20, stream)
+        us, _ = graph_time(torch, one, 20, 2, len(Ts) * spg, stream)
         per_t[str(T)] = round(us, 3)
     log(f"[bench] per-T us/call: {per_t}")
 
@@ -179,9 +197,9 @@ def main():
     tiny = torch.zeros(1, device=dev)
 
     def fill():
-        for _ in range(20):
+        for _ in range(len(Ts) * spg):
             tiny.fill_(1.0)
-    floor_us, _ = graph_time(torch, fill, 50, 5, 20, stream)
+    floor_us, _ = graph_time(torch, fill, 20, 2, len(Ts) * spg, stream)
     log(f"[bench] launch floor (1-element fill kernel, graph): {floor_us:.3f} us")
 
     traffic = None
@@ -194,6 +212,14 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
                 "kernel": "reduce_norm_kernel<Bf16, W=4, 1 pack/lane, no prefetch> (row-resident)",
                 "bytes_per_launch": bytes_per_launch, "us_per_launch": round(us_per_call, 4)}
+
+    large_t = None
+    if not args.no_large_t:
+        c3 = WORKLOADS["c3"]
+        log("[bench] prefill W=8 [8192, 8192] (split kernel)")
+        large_t = dict(time_rms(torch, arrms, workloads, c3, 8192, dev, stream),
+                       workload="W=8 partials [8192, 8192] bf16, eps 1e-5, split kernel")
+        log(f"[bench]   {large_t}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -214,12 +240,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "c2 decode sweep: W=4 partials [T,4096] bf16, Gemma RMSNorm, "
                                "eps 1e-6, T in {1,2,4,8,16,21,22,32,64,80}, row-resident kernel; "
-                               "one step = 10 fused calls replayed from a HIP graph",
+                               "one step = 10 fused calls, graph-replayed",
                    "W": W, "H": H, "T": list(Ts), "calls_per_step": len(Ts),
                    "per_T_us_per_call": per_t,
-                   "launch_floor_us": round(floor_us, 3)},
+                   "launch_floor_us": round(floor_us, 3),
+                   "steps_per_graph": spg,
+                   "us_per_call_one_step_per_graph": round(us_one_step_graph, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "large_t": large_t,
     }
     print(json.dumps(line), flush=True)
 
@@ -254,6 +283,61 @@ def cpu_baseline(cases, wl, seconds):
                       f"({el:.1f} s, one thread)"}
 
 
+def time_rms(torch, arrms, workloads, wl, T, dev, stream):
+    """us per call of one reduce+norm (or +FP8) workload, graph-replayed; inputs
+    rotate over three sets when they fit in 512 MiB (beyond the 256 MB Infinity
+    Cache), else one set."""
+    big = rms_bytes(wl.W, T, wl.H) > (1 << 29)
+    sets = 1 if big else 3
+    inps = [workloads.make_inputs(wl, T, device=dev, seed=workloads.seed_of(wl, T) + 100000 * s)
+            for s in range(sets)]
+    plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16)
+    norm = torch.empty_like(inps[0]["partials"][0])
+    res = torch.empty_like(norm)
+    quant = wl.group > 0
+    if quant:
+        q = torch.empty(norm.shape, dtype=torch.uint8, device=dev)
+        sc = torch.empty((T, wl.H // wl.group), dtype=torch.float32, device=dev)
+    n_calls = 2 if big else 20
+
+    def call():
+        for i in range(n_calls):
+            inp = inps[i % len(inps)]
+            if quant:
+                arrms.ar_rms_quant_run(plan, inp["partials"], inp["residual"], inp["weight"],
+                                       wl.eps, wl.gemma, wl.group, norm, q, sc, res,
+                                       stream=stream)
+            else:
+                arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
+                                 wl.gemma, norm, res, stream=stream)
+    us, _ = graph_time(torch, call, 10 if big else 50, 2, n_calls, stream)
+    nbytes = rms_bytes(wl.W, T, wl.H, wl.group)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out = {"us_per_call": round(us, 3), "bytes": nbytes, "GB_s": round(gbs, 1),
+           "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "kernel": "row" if plan.kernel == 0 else "split"}
+    del inps, call
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_qk(torch, arrms, workloads, wl, T, dev, stream):
+    inp = to_dev(workloads.make_qk_inputs(wl, T), dev)
+    plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16)
+    qo = torch.empty((wl.W, T, wl.q_size), dtype=torch.bfloat16, device=dev)
+    ko = torch.empty((wl.W, T, wl.kv_size), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        for _ in range(20):
+            arrms.ar_qknorm_run(plan, inp["shards"], wl.q_size, wl.kv_size, inp["q_weight"],
+                                inp["k_weight"], wl.eps, qo, ko, stream=stream)
+    us, _ = graph_time(torch, call, 50, 2, 20, stream)
+    nbytes = 2 * wl.W * T * (wl.q_size + wl.kv_size) * 2 + wl.W * (wl.q_size + wl.kv_size) * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us_per_call": round(us, 3), "bytes": nbytes, "GB_s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "kernel": "qknorm"}
+
+
 def full_report(torch, arrms, workloads, WORKLOADS, dev, stream, args):
     """Times every workload with the graph method; bytes are algorithmic."""
     out = {}
@@ -264,57 +348,10 @@ def full_report(torch, arrms, workloads, WORKLOADS, dev, stream, args):
             key = f"{name}_T{T}"
             log(f"[bench] {key}")
             if name == "c5":
-                inp = to_dev(workloads.make_qk_inputs(wl, T), dev)
-                plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16)
-                qo = torch.empty((wl.W, T, wl.q_size), dtype=torch.bfloat16, device=dev)
-                ko = torch.empty((wl.W, T, wl.kv_size), dtype=torch.bfloat16, device=dev)
-
-                def call(inp=inp, plan=plan, qo=qo, ko=ko, wl=wl):
-                    for _ in range(20):
-                        arrms.ar_qknorm_run(plan, inp["shards"], wl.q_size, wl.kv_size,
-                                            inp["q_weight"], inp["k_weight"], wl.eps, qo, ko,
-                                            stream=stream)
-                nbytes = 2 * wl.W * T * (wl.q_size + wl.kv_size) * 2 + \
-                    wl.W * (wl.q_size + wl.kv_size) * 2
-                reps, n_calls = 50, 20
+                out[key] = time_qk(torch, arrms, workloads, wl, T, dev, stream)
             else:
-                big = rms_bytes(wl.W, T, wl.H) > (1 << 29)
-                sets = 1 if big else 3
-                inps = []
-                for s in range(sets):
-                    seed = workloads.seed_of(wl, T) + 100000 * s
-                    inps.append(workloads.make_inputs(wl, T, device=dev, seed=seed))
-                plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16)
-                norm = torch.empty_like(inps[0]["partials"][0])
-                res = torch.empty_like(norm)
-                quant = wl.group > 0
-                if quant:
-                    q = torch.empty(norm.shape, dtype=torch.uint8, device=dev)
-                    sc = torch.empty((T, wl.H // wl.group), dtype=torch.float32, device=dev)
-                n_calls = 2 if big else 20
-
-                def call(inps=inps, plan=plan, norm=norm, res=res, wl=wl, quant=quant,
-                         n_calls=n_calls):
-                    for i in range(n_calls):
-                        inp = inps[i % len(inps)]
-                        if quant:
-                            arrms.ar_rms_quant_run(plan, inp["partials"], inp["residual"],
-                                                   inp["weight"], wl.eps, wl.gemma, wl.group,
-                                                   norm, q, sc, res, stream=stream)
-                        else:
-                            arrms.ar_rms_run(plan, inp["partials"], inp["residual"],
-                                             inp["weight"], wl.eps, wl.gemma, norm, res,
-                                             stream=stream)
-                nbytes = rms_bytes(wl.W, T, wl.H, wl.group)
-                reps = 10 if big else 50
-            us, _ = graph_time(torch, call, reps, 2, n_calls, stream)
-            gbs = nbytes / (us * 1e-6) / 1e9
-            out[key] = {"us_per_call": round(us, 3), "bytes": nbytes, "GB_s": round(gbs, 1),
-                        "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                        "kernel": "row" if plan.kernel == 0 else "split"}
+                out[key] = time_rms(torch, arrms, workloads, wl, T, dev, stream)
             log(f"[bench]   {out[key]}")
-            del call
-            torch.cuda.empty_cache()
     return out
 
 

@@ -217,7 +217,7 @@ enum Mode { kRow = 0, kSplit = 1, kSplitWide = 2 };
 // RES: a residual term is present (compile-time, so that every load of a row
 // is issued before the first wait).
 template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
-__global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsParams p) {
+__device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     __shared__ float wave_sums[2][kMaxBlock / 64];
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
@@ -236,8 +236,8 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsPa
         load_row<W, PPL, RES>(p, row, tid, nthr, ahead);
     }
     // weight row: loaded once per workgroup and kept (kSplitWide reloads it
-    // per row from L2 to stay within registers); converted where used, so no
-    // wait on it stands before the row's loads
+    // per row from L2 after the row's reduction, to stay within registers);
+    // converted where used, so no wait on it stands before the row's loads
     u32x4 wraw[PPL];
     auto load_weight = [&]() {
 #pragma unroll
@@ -264,7 +264,6 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsPa
 #pragma unroll
                 for (int r = 0; r < NB; ++r) cur[k][r] = u32x4{0u, 0u, 0u, 0u};
             load_row<W, PPL, RES>(p, row, tid, nthr, cur);
-            if constexpr (MODE == kSplitWide) load_weight();
         }
         const size_t base = size_t(row) * size_t(p.H) * 2;
 
@@ -307,6 +306,7 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsPa
         const float rstd = rsqrtf(total / float(p.H) + p.eps);
 
         // phase 2: normalise, weight, store; optional FP8 group epilogue
+        if constexpr (MODE == kSplitWide) load_weight();
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
             const int pk = tid + k * nthr;
@@ -350,9 +350,41 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(RmsPa
     }
 }
 
+// Kernel entry with flat arguments: the first eight (14 dwords: residual,
+// weight, H, gemma and the first four partials) are preloaded into SGPRs at
+// wave launch (built with kernarg preloading), so a row's loads start without
+// a round trip for their addresses.
+template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
+__global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
+    const uint8_t *residual, const uint8_t *weight, int32_t H, int32_t gemma,
+    const uint8_t *p0, const uint8_t *p1, const uint8_t *p2, const uint8_t *p3,
+    const uint8_t *p4, const uint8_t *p5, const uint8_t *p6, const uint8_t *p7,
+    uint8_t *norm_out, uint8_t *residual_out, uint8_t *q_out, float *scales, int64_t T,
+    float eps, int32_t group_lanes) {
+    RmsParams p;
+    p.partials[0] = p0; p.partials[1] = p1; p.partials[2] = p2; p.partials[3] = p3;
+    p.partials[4] = p4; p.partials[5] = p5; p.partials[6] = p6; p.partials[7] = p7;
+    p.residual = residual;
+    p.weight = weight;
+    p.norm_out = norm_out;
+    p.residual_out = residual_out;
+    p.q_out = q_out;
+    p.scales = scales;
+    p.T = T;
+    p.H = H;
+    p.packs = H >> 3;
+    p.eps = eps;
+    p.gemma = gemma;
+    p.group_lanes = group_lanes;
+    p.groups = QUANT ? H / (group_lanes * kPackElems) : 0;
+    reduce_norm<IO, W, PPL, MODE, QUANT, RES>(p);
+}
+
 // ------------------------------------------------------------- QK-norm
 struct QkParams {
-    const uint8_t *qkv[kMaxW];
+    // the W shard pointers as named fields: lanes pick theirs by selects, and
+    // an array here would be indexed per lane and placed in scratch memory
+    const uint8_t *x0, *x1, *x2, *x3, *x4, *x5, *x6, *x7;
     const uint8_t *q_weight;
     const uint8_t *k_weight;
     uint8_t *q_out;
@@ -370,8 +402,27 @@ struct QkParams {
 // both statistics are reduced across the workgroup together.  Lane pack idx
 // of shard r reads global weight column r * size + j, which is pack idx of
 // the concatenated weight.
+// Shard r's base pointer, chosen by selects on values held in registers.
+struct Shards {
+    const uint8_t *x0, *x1, *x2, *x3, *x4, *x5, *x6, *x7;
+    __device__ __forceinline__ const uint8_t *pick(int r) const {
+        const uintptr_t a0 = uintptr_t(x0), a1 = uintptr_t(x1), a2 = uintptr_t(x2),
+                        a3 = uintptr_t(x3), a4 = uintptr_t(x4), a5 = uintptr_t(x5),
+                        a6 = uintptr_t(x6), a7 = uintptr_t(x7);
+        uintptr_t q = a0;
+        q = r == 1 ? a1 : q;
+        q = r == 2 ? a2 : q;
+        q = r == 3 ? a3 : q;
+        q = r == 4 ? a4 : q;
+        q = r == 5 ? a5 : q;
+        q = r == 6 ? a6 : q;
+        q = r == 7 ? a7 : q;
+        return reinterpret_cast<const uint8_t *>(q);
+    }
+};
+
 template <typename IO, int PPL>
-__global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(QkParams p) {
+__device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     __shared__ float wave_sums[2][2][kMaxBlock / 64];
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
@@ -396,7 +447,7 @@ __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(QkParams p) {
                 const int per = is_q ? p.q_packs : p.kv_packs;
                 const int r = idx / per;
                 const int j = idx - r * per + (is_q ? 0 : p.q_packs);
-                xr[k] = load16_stream(p.qkv[r] + size_t(row) * p.row_bytes + size_t(j) * 16);
+                xr[k] = load16_stream(shards.pick(r) + size_t(row) * p.row_bytes + size_t(j) * 16);
             }
         }
 #pragma unroll
@@ -456,14 +507,43 @@ __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(QkParams p) {
     }
 }
 
+// Kernel entry with flat arguments; the first eight (12 dwords: the sizes and
+// the first four shards) are preloaded into SGPRs at wave launch.
+template <typename IO, int PPL>
+__global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(
+    int32_t W, int32_t q_packs, int32_t kv_packs, int32_t row_bytes, const uint8_t *x0,
+    const uint8_t *x1, const uint8_t *x2, const uint8_t *x3, const uint8_t *x4,
+    const uint8_t *x5, const uint8_t *x6, const uint8_t *x7, const uint8_t *q_weight,
+    const uint8_t *k_weight, uint8_t *q_out, uint8_t *k_out, int64_t T, float eps) {
+    QkParams p;
+    p.x0 = x0; p.x1 = x1; p.x2 = x2; p.x3 = x3;
+    p.x4 = x4; p.x5 = x5; p.x6 = x6; p.x7 = x7;
+    const Shards shards{x0, x1, x2, x3, x4, x5, x6, x7};
+    p.q_weight = q_weight;
+    p.k_weight = k_weight;
+    p.q_out = q_out;
+    p.k_out = k_out;
+    p.T = T;
+    p.W = W;
+    p.q_packs = q_packs;
+    p.kv_packs = kv_packs;
+    p.row_bytes = row_bytes;
+    p.eps = eps;
+    qknorm<IO, PPL>(p, shards);
+}
+
 // ------------------------------------------------------------- launchers
 using RmsLaunch = hipError_t (*)(const RmsParams &, unsigned, unsigned, hipStream_t);
 using QkLaunch = hipError_t (*)(const QkParams &, unsigned, unsigned, hipStream_t);
 
 template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
 hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStream_t s) {
-    RmsParams local = p;
-    void *args[] = {&local};
+    RmsParams a = p;
+    void *args[] = {&a.residual, &a.weight, &a.H, &a.gemma,
+                    &a.partials[0], &a.partials[1], &a.partials[2], &a.partials[3],
+                    &a.partials[4], &a.partials[5], &a.partials[6], &a.partials[7],
+                    &a.norm_out, &a.residual_out, &a.q_out, &a.scales, &a.T, &a.eps,
+                    &a.group_lanes};
     return hipLaunchKernel(
         reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES>),
         dim3(grid), dim3(block), args, 0, s);
@@ -471,8 +551,10 @@ hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStre
 
 template <typename IO, int PPL>
 hipError_t launch_qk(const QkParams &p, unsigned grid, unsigned block, hipStream_t s) {
-    QkParams local = p;
-    void *args[] = {&local};
+    QkParams a = p;
+    void *args[] = {&a.W, &a.q_packs, &a.kv_packs, &a.row_bytes,
+                    &a.x0, &a.x1, &a.x2, &a.x3, &a.x4, &a.x5, &a.x6, &a.x7,
+                    &a.q_weight, &a.k_weight, &a.q_out, &a.k_out, &a.T, &a.eps};
     return hipLaunchKernel(reinterpret_cast<const void *>(&qknorm_kernel<IO, PPL>), dim3(grid),
                            dim3(block), args, 0, s);
 }
@@ -639,7 +721,16 @@ extern "C" int ar_qknorm_run(const ar_rms_plan_s *plan, const void *const *qkv, 
     if (rc) return rc;
     if (plan->T == 0) return ARRMS_OK;
     QkParams p{};
-    for (int r = 0; r < plan->W; ++r) p.qkv[r] = static_cast<const uint8_t *>(qkv[r]);
+    const uint8_t *const *xs = reinterpret_cast<const uint8_t *const *>(qkv);
+    const uint8_t *first = xs[0];
+    p.x0 = first;
+    p.x1 = plan->W > 1 ? xs[1] : first;
+    p.x2 = plan->W > 2 ? xs[2] : first;
+    p.x3 = plan->W > 3 ? xs[3] : first;
+    p.x4 = plan->W > 4 ? xs[4] : first;
+    p.x5 = plan->W > 5 ? xs[5] : first;
+    p.x6 = plan->W > 6 ? xs[6] : first;
+    p.x7 = plan->W > 7 ? xs[7] : first;
     p.q_weight = static_cast<const uint8_t *>(q_weight);
     p.k_weight = static_cast<const uint8_t *>(k_weight);
     p.q_out = static_cast<uint8_t *>(q_out);
