@@ -365,3 +365,39 @@ def test_errors_leave_outputs_untouched():
         arrms.ar_rms_run(plan, [x, x[:4]], x, w, 1e-6, False, norm, res)
     torch.cuda.synchronize()
     assert bool((norm == 7.0).all()) and bool((res == 7.0).all())
+
+
+# ------------------------------------- persistent loops (more rows than workgroups)
+@pytest.mark.parametrize("W,T,H,quant", [(3, 20000, 1000, False), (2, 9000, 2048, True),
+                                         (5, 700, 16384, False), (8, 600, 12288, True)])
+def test_split_loops_over_rows(W, T, H, quant):
+    """T beyond what the device holds at once, so workgroups loop over rows
+    (with the next row prefetched; four packs per lane above 8192)."""
+    inp = cuda_inputs(GENERIC, T, W=W, H=H, seed=T + H, device_draw=True)
+    rows = sample_rows(T, 160, seed=W)
+    if quant:
+        outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"],
+                                                    inp["weight"], 1e-6, 128,
+                                                    flags=arrms.FORCE_SPLIT)
+        torch.cuda.synchronize()
+        check_quant(inp, 1e-6, False, 128, outs, rows=rows)
+    else:
+        norm, res = run_rms(inp, 1e-6, False, flags=arrms.FORCE_SPLIT)
+        torch.cuda.synchronize()
+        check_rms(inp, norm, res, 1e-6, False, rows=rows)
+
+
+def test_qk_more_tokens_than_workgroups():
+    """Beyond 65536 tokens the QK workgroups loop over tokens."""
+    W, T, q, kv = 2, 70000, 256, 256
+    inp = workloads.make_qk_inputs(WORKLOADS["c5"], T, W=W, q_size=q, kv_size=kv, seed=3,
+                                   device=DEV)
+    q_out, k_out = arrms.fused_qk_norm(inp["shards"], inp["q_weight"], inp["k_weight"], q, kv,
+                                       1e-6)
+    torch.cuda.synchronize()
+    rows = sample_rows(T, 128, seed=5)
+    idx = torch.as_tensor(rows, device=DEV)
+    sub = {"shards": [s.index_select(0, idx) for s in inp["shards"]],
+           "q_weight": inp["q_weight"], "k_weight": inp["k_weight"]}
+    check_qk(sub, q, kv, 1e-6, q_out.index_select(1, idx).contiguous(),
+             k_out.index_select(1, idx).contiguous())

@@ -184,10 +184,12 @@ struct RmsParams {
     int32_t gemma;                // weight applied as 1 + w (Gemma RMSNorm)
     int32_t group_lanes;          // group_size / 8
     int32_t groups;               // H / group_size
+    int32_t block;                // threads per workgroup (the launch's blockDim.x)
+    int32_t grid;                 // workgroups (the launch's gridDim.x)
 };
 
 // Issues the loads of one row: W partial packs and (RES) the residual pack for
-// each of the lane's PPL packs (pack pk = lane + k * blockDim).
+// each of the lane's PPL packs (pack pk = lane + k * workgroup size).
 template <int W, int PPL, bool RES>
 __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int tid, int nthr,
                                          u32x4 (&v)[PPL][W + RES]) {
@@ -220,9 +222,11 @@ template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
 __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     __shared__ float wave_sums[2][kMaxBlock / 64];
     const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
+    // launch shape from the arguments: reading blockDim/gridDim goes through
+    // the dispatch packet in memory
+    const int nthr = p.block;
     const int nwaves = nthr >> 6;
-    const int64_t stride = gridDim.x;
+    const int64_t stride = p.grid;
     int64_t row = blockIdx.x;    // < T: the launcher never starts more workgroups than rows
 
     constexpr int NB = W + RES;      // packs loaded per lane pack: partials, residual
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
     const uint8_t *p0, const uint8_t *p1, const uint8_t *p2, const uint8_t *p3,
     const uint8_t *p4, const uint8_t *p5, const uint8_t *p6, const uint8_t *p7,
     uint8_t *norm_out, uint8_t *residual_out, uint8_t *q_out, float *scales, int64_t T,
-    float eps, int32_t group_lanes) {
+    float eps, int32_t group_lanes, int32_t block, int32_t grid) {
     RmsParams p;
     p.partials[0] = p0; p.partials[1] = p1; p.partials[2] = p2; p.partials[3] = p3;
     p.partials[4] = p4; p.partials[5] = p5; p.partials[6] = p6; p.partials[7] = p7;
@@ -377,6 +381,8 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
     p.gemma = gemma;
     p.group_lanes = group_lanes;
     p.groups = QUANT ? H / (group_lanes * kPackElems) : 0;
+    p.block = block;
+    p.grid = grid;
     reduce_norm<IO, W, PPL, MODE, QUANT, RES>(p);
 }
 
@@ -395,6 +401,8 @@ struct QkParams {
     int32_t kv_packs;             // kv_size / 8
     int32_t row_bytes;            // (q_size + 2 kv_size) * 2
     float eps;
+    int32_t block;                // threads per workgroup (the launch's blockDim.x)
+    int32_t grid;                 // workgroups (the launch's gridDim.x)
 };
 
 // One workgroup per token.  Lanes cover the W shards' q packs first, then
@@ -405,70 +413,86 @@ struct QkParams {
 // Shard r's base pointer, chosen by selects on values held in registers.
 struct Shards {
     const uint8_t *x0, *x1, *x2, *x3, *x4, *x5, *x6, *x7;
+    template <int W>
     __device__ __forceinline__ const uint8_t *pick(int r) const {
-        const uintptr_t a0 = uintptr_t(x0), a1 = uintptr_t(x1), a2 = uintptr_t(x2),
-                        a3 = uintptr_t(x3), a4 = uintptr_t(x4), a5 = uintptr_t(x5),
-                        a6 = uintptr_t(x6), a7 = uintptr_t(x7);
-        uintptr_t q = a0;
-        q = r == 1 ? a1 : q;
-        q = r == 2 ? a2 : q;
-        q = r == 3 ? a3 : q;
-        q = r == 4 ? a4 : q;
-        q = r == 5 ? a5 : q;
-        q = r == 6 ? a6 : q;
-        q = r == 7 ? a7 : q;
+        const uintptr_t a[kMaxW] = {uintptr_t(x0), uintptr_t(x1), uintptr_t(x2), uintptr_t(x3),
+                                    uintptr_t(x4), uintptr_t(x5), uintptr_t(x6), uintptr_t(x7)};
+        uintptr_t q = a[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i) q = r == i ? a[i] : q;
         return reinterpret_cast<const uint8_t *>(q);
     }
 };
 
-template <typename IO, int PPL>
+// LOOP: workgroups loop over tokens (more tokens than workgroups); without it
+// every workgroup handles exactly one token in straight-line code.
+template <typename IO, int W, int PPL, bool LOOP>
 __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     __shared__ float wave_sums[2][2][kMaxBlock / 64];
     const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
+    const int nthr = p.block;     // launch shape from the arguments (see reduce_norm)
     const int nwaves = nthr >> 6;
-    const int nq = p.W * p.q_packs;
-    const int n = nq + p.W * p.kv_packs;
+    const int nq = W * p.q_packs;
+    const int n = nq + W * p.kv_packs;
     const int q_size = p.q_packs * 8;
     const int kv_size = p.kv_packs * 8;
 
+    // Row-independent lane layout, worked out once: shard r (by comparisons,
+    // no integer division), the pack's column in the shard row, the weight
+    // pack, and the output row offset.
+    bool valid[PPL], is_q[PPL];
+    const uint8_t *src[PPL];
+    int col[PPL], widx[PPL];
+    size_t out_off[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+        const int pk = tid + k * nthr;
+        valid[k] = pk < n;
+        is_q[k] = pk < nq;
+        const int idx = is_q[k] ? pk : pk - nq;
+        const int per = is_q[k] ? p.q_packs : p.kv_packs;
+        int r = 0;
+#pragma unroll
+        for (int i = 1; i < W; ++i) r += idx >= i * per ? 1 : 0;
+        const int j = idx - r * per;
+        widx[k] = idx;
+        col[k] = j + (is_q[k] ? 0 : p.q_packs);
+        src[k] = shards.pick<W>(r);
+        out_off[k] = size_t(r) * size_t(p.T) * size_t(is_q[k] ? q_size : kv_size) * 2 +
+                     size_t(j) * 16;
+    }
+
+    int64_t row = blockIdx.x;     // < T: the launcher never starts more workgroups than rows
+    u32x4 xr[PPL], wr[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+        xr[k] = u32x4{0u, 0u, 0u, 0u};
+        if (valid[k]) xr[k] = load16_stream(src[k] + size_t(row) * p.row_bytes + size_t(col[k]) * 16);
+    }
+    // weights: loaded once (the same for every token), after the first loads
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+        wr[k] = u32x4{0u, 0u, 0u, 0u};
+        if (valid[k]) wr[k] = load16((is_q[k] ? p.q_weight : p.k_weight) + size_t(widx[k]) * 16);
+    }
+
     int parity = 0;
-    for (int64_t row = blockIdx.x; row < p.T; row += gridDim.x, parity ^= 1) {
-        u32x4 xr[PPL], wr[PPL];
-        // loads first (activations, then weights), arithmetic after
-#pragma unroll
-        for (int k = 0; k < PPL; ++k) {
-            const int pk = tid + k * nthr;
-            xr[k] = u32x4{0u, 0u, 0u, 0u};
-            wr[k] = u32x4{0u, 0u, 0u, 0u};
-            if (pk < n) {
-                const bool is_q = pk < nq;
-                const int idx = is_q ? pk : pk - nq;
-                const int per = is_q ? p.q_packs : p.kv_packs;
-                const int r = idx / per;
-                const int j = idx - r * per + (is_q ? 0 : p.q_packs);
-                xr[k] = load16_stream(shards.pick(r) + size_t(row) * p.row_bytes + size_t(j) * 16);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < PPL; ++k) {
-            const int pk = tid + k * nthr;
-            if (pk < n) {
-                const bool is_q = pk < nq;
-                const int idx = is_q ? pk : pk - nq;
-                wr[k] = load16((is_q ? p.q_weight : p.k_weight) + size_t(idx) * 16);
-            }
-        }
+    for (;;) {
         float x[PPL][8];
         float ssq = 0.0f, ssk = 0.0f;
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
-            const int pk = tid + k * nthr;
             unpack8<IO>(xr[k], x[k]);
             float s = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) s = __builtin_fmaf(x[k][i], x[k][i], s);
-            if (pk < nq) ssq += s; else ssk += s;
+            if (is_q[k]) ssq += s; else ssk += s;
+        }
+        const int64_t next = row + p.grid;
+        if (LOOP && next < p.T) {
+#pragma unroll
+            for (int k = 0; k < PPL; ++k)
+                if (valid[k]) xr[k] = load16_stream(src[k] + size_t(next) * p.row_bytes + size_t(col[k]) * 16);
         }
         const float wq = wave_sum(ssq);
         const float wk = wave_sum(ssk);
@@ -482,39 +506,36 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
             tq += wave_sums[parity][0][i];
             tk += wave_sums[parity][1][i];
         }
-        const float rq = rsqrtf(tq / float(p.W * q_size) + p.eps);
-        const float rk = rsqrtf(tk / float(p.W * kv_size) + p.eps);
+        const float rq = rsqrtf(tq / float(W * q_size) + p.eps);
+        const float rk = rsqrtf(tk / float(W * kv_size) + p.eps);
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
-            const int pk = tid + k * nthr;
-            if (pk < n) {
-                const bool is_q = pk < nq;
-                const int idx = is_q ? pk : pk - nq;
-                const int per = is_q ? p.q_packs : p.kv_packs;
-                const int r = idx / per;
-                const int j = idx - r * per;
+            if (valid[k]) {
                 float wv[8];
                 unpack8<IO>(wr[k], wv);
-                const float rs = is_q ? rq : rk;
+                const float rs = is_q[k] ? rq : rk;
                 float y[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) y[i] = (x[k][i] * rs) * wv[i];
-                uint8_t *out = is_q ? p.q_out + ((size_t(r) * p.T + row) * q_size) * 2
-                                    : p.k_out + ((size_t(r) * p.T + row) * kv_size) * 2;
-                store16(out + size_t(j) * 16, pack8<IO>(y));
+                const size_t row_off = size_t(row) * size_t(is_q[k] ? q_size : kv_size) * 2;
+                store16((is_q[k] ? p.q_out : p.k_out) + out_off[k] + row_off, pack8<IO>(y));
             }
         }
+        if (!LOOP || next >= p.T) break;
+        row = next;
+        parity ^= 1;
     }
 }
 
 // Kernel entry with flat arguments; the first eight (12 dwords: the sizes and
 // the first four shards) are preloaded into SGPRs at wave launch.
-template <typename IO, int PPL>
+template <typename IO, int W, int PPL, bool LOOP>
 __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(
-    int32_t W, int32_t q_packs, int32_t kv_packs, int32_t row_bytes, const uint8_t *x0,
+    int32_t shards_used, int32_t q_packs, int32_t kv_packs, int32_t row_bytes, const uint8_t *x0,
     const uint8_t *x1, const uint8_t *x2, const uint8_t *x3, const uint8_t *x4,
     const uint8_t *x5, const uint8_t *x6, const uint8_t *x7, const uint8_t *q_weight,
-    const uint8_t *k_weight, uint8_t *q_out, uint8_t *k_out, int64_t T, float eps) {
+    const uint8_t *k_weight, uint8_t *q_out, uint8_t *k_out, int64_t T, float eps, int32_t block,
+    int32_t grid) {
     QkParams p;
     p.x0 = x0; p.x1 = x1; p.x2 = x2; p.x3 = x3;
     p.x4 = x4; p.x5 = x5; p.x6 = x6; p.x7 = x7;
@@ -524,12 +545,14 @@ __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(
     p.q_out = q_out;
     p.k_out = k_out;
     p.T = T;
-    p.W = W;
+    p.W = shards_used;
     p.q_packs = q_packs;
     p.kv_packs = kv_packs;
     p.row_bytes = row_bytes;
     p.eps = eps;
-    qknorm<IO, PPL>(p, shards);
+    p.block = block;
+    p.grid = grid;
+    qknorm<IO, W, PPL, LOOP>(p, shards);
 }
 
 // ------------------------------------------------------------- launchers
@@ -539,24 +562,29 @@ using QkLaunch = hipError_t (*)(const QkParams &, unsigned, unsigned, hipStream_
 template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
 hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStream_t s) {
     RmsParams a = p;
+    a.block = int32_t(block);
+    a.grid = int32_t(grid);
     void *args[] = {&a.residual, &a.weight, &a.H, &a.gemma,
                     &a.partials[0], &a.partials[1], &a.partials[2], &a.partials[3],
                     &a.partials[4], &a.partials[5], &a.partials[6], &a.partials[7],
                     &a.norm_out, &a.residual_out, &a.q_out, &a.scales, &a.T, &a.eps,
-                    &a.group_lanes};
+                    &a.group_lanes, &a.block, &a.grid};
     return hipLaunchKernel(
         reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES>),
         dim3(grid), dim3(block), args, 0, s);
 }
 
-template <typename IO, int PPL>
+template <typename IO, int W, int PPL, bool LOOP>
 hipError_t launch_qk(const QkParams &p, unsigned grid, unsigned block, hipStream_t s) {
     QkParams a = p;
+    a.block = int32_t(block);
+    a.grid = int32_t(grid);
     void *args[] = {&a.W, &a.q_packs, &a.kv_packs, &a.row_bytes,
                     &a.x0, &a.x1, &a.x2, &a.x3, &a.x4, &a.x5, &a.x6, &a.x7,
-                    &a.q_weight, &a.k_weight, &a.q_out, &a.k_out, &a.T, &a.eps};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&qknorm_kernel<IO, PPL>), dim3(grid),
-                           dim3(block), args, 0, s);
+                    &a.q_weight, &a.k_weight, &a.q_out, &a.k_out, &a.T, &a.eps, &a.block,
+                    &a.grid};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&qknorm_kernel<IO, W, PPL, LOOP>),
+                           dim3(grid), dim3(block), args, 0, s);
 }
 
 // A kernel variant: its launcher and its symbol (for the occupancy query).
@@ -609,14 +637,34 @@ Variant pick_rms(int dtype, int W, int mode, bool quant, bool res) {
                                : pick_io<Fp16>(W, mode, quant, res);
 }
 
-template <typename IO>
+template <typename IO, int W, bool LOOP>
 QkLaunch pick_qk_ppl(int ppl) {
     switch (ppl) {
-    case 1: return &launch_qk<IO, 1>;
-    case 2: return &launch_qk<IO, 2>;
-    case 4: return &launch_qk<IO, 4>;
+    case 1: return &launch_qk<IO, W, 1, LOOP>;
+    case 2: return &launch_qk<IO, W, 2, LOOP>;
+    case 4: return &launch_qk<IO, W, 4, LOOP>;
     default: return nullptr;
     }
+}
+
+template <typename IO, bool LOOP>
+QkLaunch pick_qk_w(int W, int ppl) {
+    switch (W) {
+    case 1: return pick_qk_ppl<IO, 1, LOOP>(ppl);
+    case 2: return pick_qk_ppl<IO, 2, LOOP>(ppl);
+    case 3: return pick_qk_ppl<IO, 3, LOOP>(ppl);
+    case 4: return pick_qk_ppl<IO, 4, LOOP>(ppl);
+    case 5: return pick_qk_ppl<IO, 5, LOOP>(ppl);
+    case 6: return pick_qk_ppl<IO, 6, LOOP>(ppl);
+    case 7: return pick_qk_ppl<IO, 7, LOOP>(ppl);
+    case 8: return pick_qk_ppl<IO, 8, LOOP>(ppl);
+    default: return nullptr;
+    }
+}
+
+template <typename IO>
+QkLaunch pick_qk(int W, int ppl, bool loop) {
+    return loop ? pick_qk_w<IO, true>(W, ppl) : pick_qk_w<IO, false>(W, ppl);
 }
 
 // Workgroups of the split kernel that the device holds at once (CUs times
@@ -668,16 +716,25 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
     p.gemma = gemma ? 1 : 0;
     p.group_lanes = quant ? group_size / kPackElems : 1;
     p.groups = quant ? int32_t(plan->H / group_size) : 0;
+    // The split plan launches min(T, resident workgroups); when every row gets
+    // its own workgroup the straight-line row body is used (the loop costs
+    // latency and has nothing to overlap).
     const bool split = plan->kernel == ARRMS_KERNEL_SPLIT;
-    const int mode = !split ? kRow : (plan->ppl == 1 ? kSplit : kSplitWide);
-    Variant v = pick_rms(plan->dtype, plan->W, mode, quant, residual != nullptr);
+    int mode = !split ? kRow : (plan->ppl == 1 ? kSplit : kSplitWide);
+    const bool res = residual != nullptr;
+    Variant v = pick_rms(plan->dtype, plan->W, mode, quant, res);
     if (v.launch == nullptr)
         return fail(ARRMS_ENOTSUP, "no kernel for W=%d, %d packs per lane", plan->W, plan->ppl);
     int64_t grid = plan->T;
     if (split) {
         const int resident = resident_grid(v.symbol, plan->block);
         if (resident <= 0) return fail(ARRMS_EHIP, "device occupancy query failed");
-        if (grid > resident) grid = resident;
+        if (grid > resident) {
+            grid = resident;
+        } else if (mode == kSplit) {
+            mode = kRow;
+            v = pick_rms(plan->dtype, plan->W, mode, quant, res);
+        }
     }
     hipError_t e = v.launch(p, unsigned(grid), unsigned(plan->block), static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -742,10 +799,13 @@ extern "C" int ar_qknorm_run(const ar_rms_plan_s *plan, const void *const *qkv, 
     p.row_bytes = int32_t(plan->H * 2);
     p.eps = eps;
     Shape s = qk_shape(plan->W, q_size, kv_size);
-    QkLaunch fn = plan->dtype == ARRMS_BF16 ? pick_qk_ppl<Bf16>(s.ppl) : pick_qk_ppl<Fp16>(s.ppl);
-    if (fn == nullptr) return fail(ARRMS_ENOTSUP, "no QK kernel for %d packs per lane", s.ppl);
     // one workgroup per token; beyond 65536 tokens workgroups loop over tokens
-    const int64_t grid = plan->T < 65536 ? plan->T : 65536;
+    const int64_t max_grid = 65536;
+    const bool loop = plan->T > max_grid;
+    const int64_t grid = loop ? max_grid : plan->T;
+    QkLaunch fn = plan->dtype == ARRMS_BF16 ? pick_qk<Bf16>(plan->W, s.ppl, loop)
+                                            : pick_qk<Fp16>(plan->W, s.ppl, loop);
+    if (fn == nullptr) return fail(ARRMS_ENOTSUP, "no QK kernel for %d packs per lane", s.ppl);
     hipError_t e = fn(p, unsigned(grid), unsigned(s.block), static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(ARRMS_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
