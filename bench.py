@@ -203,15 +203,18 @@ def main():
     log(f"[bench] launch floor (1-element fill kernel, graph): {floor_us:.3f} us")
 
     traffic = None
+    rocprof_us = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
         if rec.get("kernel_source_sha") == kernel_source_sha():
             traffic = rec.get("traffic_bytes_per_launch")
+            rocprof_us = rec.get("rocprof_mean_duration_us")
 
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
                 "kernel": "reduce_norm_kernel<Bf16, W=4, 1 pack/lane, no prefetch> (row-resident)",
-                "bytes_per_launch": bytes_per_launch, "us_per_launch": round(us_per_call, 4)}
+                "bytes_per_launch": bytes_per_launch, "us_per_launch": round(us_per_call, 4),
+                "rocprof_us_per_launch": rocprof_us}
 
     large_t = None
     if not args.no_large_t:
