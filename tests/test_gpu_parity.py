@@ -401,3 +401,23 @@ def test_qk_more_tokens_than_workgroups():
            "q_weight": inp["q_weight"], "k_weight": inp["k_weight"]}
     check_qk(sub, q, kv, 1e-6, q_out.index_select(1, idx).contiguous(),
              k_out.index_select(1, idx).contiguous())
+
+
+@pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
+def test_quant_tiny_and_zero_scales(flags):
+    """Groups whose scale is subnormal (amax/448 below 2^-126, reciprocal beyond
+    fp32), a group of zero weights (scale 0, codes 0) and ordinary groups."""
+    W, T, H, G = 2, 9, 1024, 128
+    inp = cuda_inputs(WORKLOADS["c4"], T, W=W, H=H, seed=11)
+    w = inp["weight"].float()
+    w[:G] = w[:G] * 1e-37          # tiny: normalised values ~1e-37
+    w[G:2 * G] = 0.0               # zero group
+    w[2 * G:3 * G] = w[2 * G:3 * G] * 3e-36
+    inp["weight"] = w.to(torch.bfloat16)
+    outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"], inp["weight"],
+                                                1e-6, G, flags=flags)
+    torch.cuda.synchronize()
+    check_quant(inp, 1e-6, False, G, outs)
+    scales = outs[2].cpu().numpy()
+    assert np.all(scales[:, 1] == 0) and np.all(scales[:, 0] < 2.0 ** -126)
+    assert np.all(outs[1].view(torch.uint8).cpu().numpy()[:, G:2 * G] == 0)

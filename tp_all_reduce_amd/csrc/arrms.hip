@@ -12,7 +12,8 @@
 //            one barrier across the workgroup's wavefronts;
 //   phase 2  rstd, (1 + w) or w, 16-bit norm_out store, and optionally the
 //            per-group FP8 epilogue (group amax by DPP within the lanes that
-//            hold the group, scale = amax / 448, E4M3FN codes).
+//            hold the group, scale = amax / 448, E4M3FN codes by the hardware
+//            conversion).
 // The row stays in registers between the phases, so HBM sees each input once
 // and each output once: (W + 2) * T * H * 2 bytes plus the weight.
 //
@@ -153,19 +154,13 @@ __device__ __forceinline__ float group_max(float v, int lanes) {
     return v;
 }
 
-// fp32 -> OCP FP8 E4M3FN, round to nearest even, saturating at +-448, NaN to
-// 0x7F.  Normal range: keep 3 fraction bits of the fp32 pattern with
-// nearest-even rounding and re-bias the exponent from 127 to 7; below 2^-6 the
-// grid is the subnormal quantum 2^-9.
-__device__ __forceinline__ uint32_t to_e4m3(float v) {
-    if (v != v) return 0x7Fu;
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fminf(fabsf(v), 448.0f);
-    const uint32_t sub = uint32_t(__builtin_rintf(a * 512.0f));
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    const uint32_t nrm = (b >> 20) - (120u << 3);
-    return sign | (a < 0.015625f ? sub : nrm);
+// Four fp32 values -> four OCP FP8 E4M3FN codes (byte i = value i), rounded to
+// nearest even by v_cvt_pk_fp8_f32.  The instruction turns magnitudes that
+// round beyond 448 into NaN (and NaN into 0xFF); the callers only pass values
+// of magnitude <= 448 * (1 + 2^-22), which round to at most 448.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
 // ------------------------------------------------------- reduce + RMSNorm
@@ -334,16 +329,27 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
                 const float scale = amax / 448.0f;
                 uint32_t lo = 0, hi = 0;
                 if (scale != 0.0f) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) lo |= to_e4m3(y[i] / scale) << (8 * i);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) hi |= to_e4m3(y[4 + i] / scale) << (8 * i);
+                    // One division per lane, then products: y * (1 / scale) is within
+                    // one fp32 rounding of y / scale.  Since |y| <= amax, every
+                    // quotient is at most 448 * (1 + 3 * 2^-24) and rounds to at
+                    // most 448: no saturation step is needed.  A scale below about
+                    // 2^-128 has no finite reciprocal; those groups divide.
+                    const float inv = 1.0f / scale;
+                    if (__builtin_expect(inv <= 3.40282347e38f, 1)) {
+                        lo = pack4_e4m3(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
+                        hi = pack4_e4m3(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
+                    } else {
+                        lo = pack4_e4m3(y[0] / scale, y[1] / scale, y[2] / scale, y[3] / scale);
+                        hi = pack4_e4m3(y[4] / scale, y[5] / scale, y[6] / scale, y[7] / scale);
+                    }
                 }
                 if (valid) {
                     *reinterpret_cast<u32x2 *>(p.q_out + size_t(row) * p.H + size_t(pk) * 8) =
                         u32x2{lo, hi};
+                    // group_lanes is a power of two: the group index is a shift
                     if ((pk & (p.group_lanes - 1)) == 0)
-                        p.scales[size_t(row) * p.groups + pk / p.group_lanes] = scale;
+                        p.scales[size_t(row) * p.groups + (pk >> __builtin_ctz(p.group_lanes))] =
+                            scale;
                 }
             }
         }
