@@ -49,8 +49,9 @@ def _load():
         # ORACLE_LIB lets the planted-mistake tests run the pins against a
         # deliberately broken copy of the oracle
         path = os.environ.get("ORACLE_LIB") or LIB
-        if path == LIB and not os.path.exists(LIB):
-            build(force=False)
+        if path == LIB and (not os.path.exists(LIB)
+                            or os.path.getmtime(LIB) < os.path.getmtime(SRC)):
+            build(force=True)
         _lib = open_library(path)
     return _lib
 
@@ -71,14 +72,14 @@ def open_library(path: str):
     lib.oracle_encode.restype = ctypes.c_uint32
     lib.oracle_one_stage.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.oracle_one_stage.restype = ctypes.c_int
-    lib.oracle_ar_rms.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int, u16pp, u16p, u16p,
-                                  ctypes.c_float, ctypes.c_int, u16p, u16p, dp]
-    lib.oracle_ar_rms.restype = ctypes.c_int
-    lib.oracle_ar_rms_quant.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int, u16pp, u16p,
-                                        u16p, ctypes.c_float, ctypes.c_int, i64, u16p,
-                                        ctypes.POINTER(ctypes.c_uint8),
-                                        ctypes.POINTER(ctypes.c_float), u16p, dp]
-    lib.oracle_ar_rms_quant.restype = ctypes.c_int
+    lib.oracle_ar_rms_ex.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int, u16pp, u16p, u16p,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, u16p, u16p, dp]
+    lib.oracle_ar_rms_ex.restype = ctypes.c_int
+    lib.oracle_ar_rms_quant_ex.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int, u16pp, u16p,
+                                           u16p, ctypes.c_float, ctypes.c_int, ctypes.c_int, i64,
+                                           u16p, ctypes.POINTER(ctypes.c_uint8),
+                                           ctypes.POINTER(ctypes.c_float), u16p, dp]
+    lib.oracle_ar_rms_quant_ex.restype = ctypes.c_int
     lib.oracle_qknorm.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int, u16pp,
                                   u16p, u16p, ctypes.c_float, u16p, u16p, dp, dp]
     lib.oracle_qknorm.restype = ctypes.c_int
@@ -145,7 +146,7 @@ def one_stage(W: int, numel: int, hidden: int, fmt: int, fully_connected: int = 
 
 
 def ar_rms(partials, residual, weight, eps: float, gemma: bool, fmt: int = BF16,
-           want_exact: bool = True):
+           want_exact: bool = True, round_reduced: bool = False):
     """Returns (norm_out bits, residual_out bits, exact fp64 or None).
 
     partials: sequence of W uint16 arrays [T, H]; residual: [T, H] or None (no
@@ -158,17 +159,18 @@ def ar_rms(partials, residual, weight, eps: float, gemma: bool, fmt: int = BF16,
     norm = np.empty((T, H), np.uint16)
     res_out = np.empty((T, H), np.uint16)
     exact = np.empty((T, H), np.float64) if want_exact else None
-    rc = _load().oracle_ar_rms(W, T, H, fmt, _ptr_array(partials),
-                               _ptr(residual, ctypes.c_uint16), _ptr(weight, ctypes.c_uint16),
-                               float(eps), int(bool(gemma)), _ptr(norm, ctypes.c_uint16),
-                               _ptr(res_out, ctypes.c_uint16), _ptr(exact, ctypes.c_double))
+    rc = _load().oracle_ar_rms_ex(W, T, H, fmt, _ptr_array(partials),
+                                  _ptr(residual, ctypes.c_uint16), _ptr(weight, ctypes.c_uint16),
+                                  float(eps), int(bool(gemma)), int(bool(round_reduced)),
+                                  _ptr(norm, ctypes.c_uint16), _ptr(res_out, ctypes.c_uint16),
+                                  _ptr(exact, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle_ar_rms rejected its arguments")
     return norm, res_out, exact
 
 
 def ar_rms_quant(partials, residual, weight, eps: float, gemma: bool, group: int,
-                 fmt: int = BF16, want_exact: bool = True):
+                 fmt: int = BF16, want_exact: bool = True, round_reduced: bool = False):
     """Returns (norm_out bits, codes u8, scales f32, residual_out bits, exact)."""
     partials = [_u16(p) for p in partials]
     W = len(partials)
@@ -180,12 +182,13 @@ def ar_rms_quant(partials, residual, weight, eps: float, gemma: bool, group: int
     scales = np.empty((T, H // group if group > 0 else 0), np.float32)
     res_out = np.empty((T, H), np.uint16)
     exact = np.empty((T, H), np.float64) if want_exact else None
-    rc = _load().oracle_ar_rms_quant(W, T, H, fmt, _ptr_array(partials),
-                                     _ptr(residual, ctypes.c_uint16),
-                                     _ptr(weight, ctypes.c_uint16), float(eps),
-                                     int(bool(gemma)), int(group), _ptr(norm, ctypes.c_uint16),
-                                     _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_float),
-                                     _ptr(res_out, ctypes.c_uint16), _ptr(exact, ctypes.c_double))
+    rc = _load().oracle_ar_rms_quant_ex(W, T, H, fmt, _ptr_array(partials),
+                                        _ptr(residual, ctypes.c_uint16),
+                                        _ptr(weight, ctypes.c_uint16), float(eps),
+                                        int(bool(gemma)), int(bool(round_reduced)), int(group),
+                                        _ptr(norm, ctypes.c_uint16), _ptr(codes, ctypes.c_uint8),
+                                        _ptr(scales, ctypes.c_float), _ptr(res_out, ctypes.c_uint16),
+                                        _ptr(exact, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle_ar_rms_quant rejected its arguments")
     return norm, codes, scales, res_out, exact

@@ -198,18 +198,23 @@ int oracle_one_stage(int W, int64_t numel, int64_t hidden, int f, int fully_conn
 /* ------------------------------------------------------------------------- */
 
 /* Fills, for every token row t:
- *   acc[h]          = fl32(...fl32(fl32(P_0 + P_1) + P_2)... + P_{W-1}) + R)  (fp32)
+ *   sum[h]          = fl32(...fl32(fl32(P_0 + P_1) + P_2)... + P_{W-1})     (fp32)
+ *   acc[h]          = fl32(sum[h] + R)      or, with round_reduced,
+ *                     fl32(round(sum[h]) + R)
  *   residual_out    = round(acc)
  *   rstd            = 1 / sqrt(sum_h acc[h]^2 / H + eps)                     (fp64)
  *   exact[t,h]      = acc[h] * rstd * (gemma ? 1 + w[h] : w[h])               (fp64)
  *   norm_out        = round(exact)
+ * round_reduced reproduces the unfused path, whose all-reduce returns the sum as
+ * a 16-bit tensor before the residual is added and the row normalised ([54787],
+ * "Key source excerpts": the fallback of fused_allreduce_gemma_rms_norm).
  * `partials` is a host array of W pointers to [T,H] bit patterns; residual may be
  * NULL (no residual term, no residual_out); residual_out and exact may be NULL.
  * Returns 0, or -1 on bad arguments. */
-int oracle_ar_rms(int W, int64_t T, int64_t H, int f,
-                  const uint16_t *const *partials, const uint16_t *residual,
-                  const uint16_t *weight, float eps, int gemma,
-                  uint16_t *norm_out, uint16_t *residual_out, double *exact)
+int oracle_ar_rms_ex(int W, int64_t T, int64_t H, int f,
+                     const uint16_t *const *partials, const uint16_t *residual,
+                     const uint16_t *weight, float eps, int gemma, int round_reduced,
+                     uint16_t *norm_out, uint16_t *residual_out, double *exact)
 {
     if (W < 1 || T < 0 || H <= 0 || (f != ORC_BF16 && f != ORC_FP16)) return -1;
     float *acc = malloc((size_t)H * sizeof *acc);
@@ -220,6 +225,7 @@ int oracle_ar_rms(int W, int64_t T, int64_t H, int f,
             float s = (float)oracle_decode(f, partials[0][row + h]);
             for (int r = 1; r < W; ++r)
                 s = s + (float)oracle_decode(f, partials[r][row + h]);
+            if (round_reduced) s = (float)oracle_round(f, (double)s);
             if (residual) s = s + (float)oracle_decode(f, residual[row + h]);
             acc[h] = s;
             if (residual_out) residual_out[row + h] = (uint16_t)oracle_encode(f, (double)s);
@@ -239,6 +245,15 @@ int oracle_ar_rms(int W, int64_t T, int64_t H, int f,
     return 0;
 }
 
+int oracle_ar_rms(int W, int64_t T, int64_t H, int f,
+                  const uint16_t *const *partials, const uint16_t *residual,
+                  const uint16_t *weight, float eps, int gemma,
+                  uint16_t *norm_out, uint16_t *residual_out, double *exact)
+{
+    return oracle_ar_rms_ex(W, T, H, f, partials, residual, weight, eps, gemma, 0, norm_out,
+                            residual_out, exact);
+}
+
 /* As oracle_ar_rms, then per-group FP8 quantisation of the normalised row
  * ([54787], "Implementation breakdown" item 2: the per-group-quant variants;
  * [50802], "Key source excerpts": group quant of the RMSNorm output).
@@ -248,11 +263,11 @@ int oracle_ar_rms(int W, int64_t T, int64_t H, int f,
  *   code[h]     = E4M3FN_RNE_SAT( fl32( fl32(exact[h]) / scale ) ),  0 if scale == 0
  *   scales[t,g] = scale
  * norm_out may be NULL (codes only). */
-int oracle_ar_rms_quant(int W, int64_t T, int64_t H, int f,
-                        const uint16_t *const *partials, const uint16_t *residual,
-                        const uint16_t *weight, float eps, int gemma, int64_t group,
-                        uint16_t *norm_out, uint8_t *q_out, float *scales,
-                        uint16_t *residual_out, double *exact)
+int oracle_ar_rms_quant_ex(int W, int64_t T, int64_t H, int f,
+                           const uint16_t *const *partials, const uint16_t *residual,
+                           const uint16_t *weight, float eps, int gemma, int round_reduced,
+                           int64_t group, uint16_t *norm_out, uint8_t *q_out, float *scales,
+                           uint16_t *residual_out, double *exact)
 {
     if (W < 1 || W > 64 || H <= 0 || group <= 0 || H % group != 0) return -1;
     double *row_exact = malloc((size_t)H * sizeof *row_exact);
@@ -262,9 +277,9 @@ int oracle_ar_rms_quant(int W, int64_t T, int64_t H, int f,
     for (int64_t t = 0; t < T && rc == 0; ++t) {
         const uint16_t *prow[64];
         for (int r = 0; r < W; ++r) prow[r] = partials[r] + t * H;
-        rc = oracle_ar_rms(W, 1, H, f, prow, residual ? residual + t * H : NULL,
-                           weight, eps, gemma, row_norm,
-                           residual_out ? residual_out + t * H : NULL, row_exact);
+        rc = oracle_ar_rms_ex(W, 1, H, f, prow, residual ? residual + t * H : NULL,
+                              weight, eps, gemma, round_reduced, row_norm,
+                              residual_out ? residual_out + t * H : NULL, row_exact);
         if (rc) break;
         if (norm_out) memcpy(norm_out + t * H, row_norm, (size_t)H * sizeof *row_norm);
         if (exact) memcpy(exact + t * H, row_exact, (size_t)H * sizeof *row_exact);
@@ -291,6 +306,16 @@ int oracle_ar_rms_quant(int W, int64_t T, int64_t H, int f,
     free(row_exact);
     free(row_norm);
     return rc;
+}
+
+int oracle_ar_rms_quant(int W, int64_t T, int64_t H, int f,
+                        const uint16_t *const *partials, const uint16_t *residual,
+                        const uint16_t *weight, float eps, int gemma, int64_t group,
+                        uint16_t *norm_out, uint8_t *q_out, float *scales,
+                        uint16_t *residual_out, double *exact)
+{
+    return oracle_ar_rms_quant_ex(W, T, H, f, partials, residual, weight, eps, gemma, 0, group,
+                                  norm_out, q_out, scales, residual_out, exact);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -310,3 +310,33 @@ def test_workload_generator_is_seeded_and_shaped():
     assert abs(s - 0.5) < 0.02
     qk = workloads.make_qk_inputs(workloads.WORKLOADS["c5"], 64)
     assert qk["shards"][0].shape == (64, 2048) and qk["q_weight"].shape == (6144,)
+
+
+# ------------------------------------- reduced sum rounded first (unfused numerics)
+def test_round_reduced_worked_case():
+    # P = {1, 2^-8}, R = 2^-9: the 16-bit all-reduce gives bf16(1 + 2^-8) = 1.0 (tie to
+    # even); adding 2^-9 then rounds back to 1.0 (without rounding first: 1.0078125)
+    P = [b16([[1.0]]), b16([[2.0 ** -8]])]
+    _, res, _ = oracle.ar_rms(P, b16([[2.0 ** -9]]), b16([1.0]), 1e-6, False, round_reduced=True)
+    assert val(res)[0, 0] == 1.0
+
+
+@pytest.mark.parametrize("W,fmt", [(2, BF16), (4, BF16), (8, BF16), (3, FP16)])
+def test_round_reduced_matches_library_rounding(W, fmt):
+    rng = np.random.default_rng(90 + W)
+    T, H = 5, 160
+    dt = torch.bfloat16 if fmt == BF16 else torch.float16
+    P = [rand_bits(rng, (T, H), dtype=dt) for _ in range(W)]
+    R = rand_bits(rng, (T, H), dtype=dt)
+    w = rand_bits(rng, (H,), 0.1, 1.0, dt)
+    norm, res, exact = oracle.ar_rms(P, R, w, 1e-5, False, fmt, round_reduced=True)
+    s = fp32_sum(P, None, fmt)
+    reduced = torch.from_numpy(s).to(dt).float().numpy()          # the 16-bit all-reduce
+    acc = (reduced + val(R, fmt).astype(np.float32)).astype(np.float32)
+    ref = torch.from_numpy(acc).to(dt).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(res, ref)
+    np.testing.assert_allclose(exact, torch_rms(acc.astype(np.float64), val(w, fmt),
+                                                float(np.float32(1e-5))), rtol=1e-13)
+    # the quant variant carries the same reading
+    n2, _, _, r2, e2 = oracle.ar_rms_quant(P, R, w, 1e-5, False, 32, fmt, round_reduced=True)
+    assert np.array_equal(r2, res) and np.array_equal(e2, exact)

@@ -17,6 +17,7 @@ PINS = ["tests/test_oracle_predicate.py", "tests/test_oracle_method.py",
 # (name, original text, planted mistake)
 MUTANTS = [
     ("residual_dropped", "if (residual) s = s + (float)", "if (0) s = s + (float)"),
+    ("round_reduced_ignored", "if (round_reduced) s = (float)oracle_round(f, (double)s);", ""),
     ("sum_in_fp64", "float s = (float)oracle_decode(f, partials[0][row + h]);",
      "double s = oracle_decode(f, partials[0][row + h]);"),
     ("gemma_sign", "gemma ? 1.0 + w : w", "gemma ? 1.0 - w : w"),
