@@ -52,10 +52,15 @@ enum {
  * "Key source excerpts": dtype bf16 or fp16). */
 enum { ARRMS_BF16 = 0, ARRMS_FP16 = 1 };
 
-/* Plan flags: override the dispatch predicate. */
+/* Plan flags. */
 enum {
-    ARRMS_FORCE_ROW = 1u << 0,   /* row-resident kernel; needs T <= 80 and H/8 <= 1024 */
-    ARRMS_FORCE_SPLIT = 1u << 1  /* split (multi-row, bandwidth) kernel; always valid */
+    ARRMS_FORCE_ROW = 1u << 0,     /* row-resident kernel; needs T <= 80 and H/8 <= 1024 */
+    ARRMS_FORCE_SPLIT = 1u << 1,   /* split (multi-row, bandwidth) kernel; always valid */
+    /* Round the W-way fp32 sum to the 16-bit format before the residual is added,
+     * as the unfused path does, whose all-reduce returns a 16-bit tensor (PR #54787
+     * page, "Key source excerpts": the fallback of fused_allreduce_gemma_rms_norm).
+     * Without it the sum stays fp32 until residual_out is rounded once. */
+    ARRMS_ROUND_REDUCED = 1u << 2
 };
 
 /* Kernel chosen by a plan (ar_rms_plan_kernel). */
@@ -99,6 +104,8 @@ int ar_rms_plan_kernel(const ar_rms_plan_s *plan);
  * _rocm_aiter_fused_allreduce_rmsnorm_impl and its fake, which returns outputs
  * shaped like the input and the residual).  For every token row t, element h:
  *   y          = (((P_0 + P_1) + ...) + P_{W-1}) + R         in fp32, this order
+ *                (with ARRMS_ROUND_REDUCED the sum of the P_r is rounded to the
+ *                16-bit format before R is added)
  *   residual_out = round_to_dtype(y)                          (nearest-even)
  *   norm_out   = round_to_dtype(y * rsqrt(sum_h y^2 / H + eps) * w_eff)
  * with w_eff = w (gemma == 0) or 1 + w (gemma != 0, Gemma RMSNorm; PR #54787

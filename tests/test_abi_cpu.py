@@ -78,7 +78,7 @@ def test_plan_dispatch_for_the_workloads():
     ((2, -1, 1024, 0, 0), arrms.EINVAL),         # T < 0
     ((2, 8, 0, 0, 0), arrms.EINVAL),             # H <= 0
     ((2, 8, 1024, 2, 0), arrms.EINVAL),          # fp32 / unknown dtype
-    ((2, 8, 1024, 0, 4), arrms.EINVAL),          # unknown flag bit
+    ((2, 8, 1024, 0, 8), arrms.EINVAL),          # unknown flag bit
     ((2, 8, 1024, 0, 3), arrms.EINVAL),          # both FORCE flags
     ((9, 8, 1024, 0, 0), arrms.ENOTSUP),         # W > 8
     ((2, 8, 1020, 0, 0), arrms.ENOTSUP),         # H % 8 != 0
@@ -90,6 +90,12 @@ def test_plan_errors(args, code):
     with pytest.raises(arrms.ArrmsError) as e:
         arrms.ar_rms_plan(*args)
     assert e.value.code == code and e.value.message
+
+
+def test_round_reduced_flag_accepted_with_any_kernel():
+    for f in (0, arrms.FORCE_ROW, arrms.FORCE_SPLIT):
+        p = arrms.ar_rms_plan(4, 8, 4096, 0, f | arrms.ROUND_REDUCED)
+        assert p.kernel == (arrms.KERNEL_SPLIT if f == arrms.FORCE_SPLIT else arrms.KERNEL_ROW)
 
 
 def test_plan_limits_accepted():

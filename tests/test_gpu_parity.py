@@ -421,3 +421,57 @@ def test_quant_tiny_and_zero_scales(flags):
     scales = outs[2].cpu().numpy()
     assert np.all(scales[:, 1] == 0) and np.all(scales[:, 0] < 2.0 ** -126)
     assert np.all(outs[1].view(torch.uint8).cpu().numpy()[:, G:2 * G] == 0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("flags,T", [(arrms.FORCE_ROW, 21), (arrms.FORCE_SPLIT, 21),
+                                     (arrms.FORCE_SPLIT, 5000)], ids=["row", "split", "split_loop"])
+def test_round_reduced_sum(flags, T, dtype):
+    """ARRMS_ROUND_REDUCED: the W-way sum is rounded to 16 bits before the residual."""
+    wl = WORKLOADS["c2"]
+    fmt = FMT[dtype]
+    inp = cuda_inputs(wl, T, dtype, seed=77 + T, device_draw=T > 1000)
+    norm, res = arrms.fused_allreduce_rms_norm(inp["partials"], inp["residual"], inp["weight"],
+                                               wl.eps, True, flags=flags, round_reduced=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(T, 128, seed=1)
+    P = [host_rows(p, rows) for p in inp["partials"]]
+    R = host_rows(inp["residual"], rows)
+    n, r, exact = oracle.ar_rms(P, R, bits(inp["weight"]), wl.eps, True, fmt, round_reduced=True)
+    assert compare.bits_equal(host_rows(res, rows), r)
+    assert compare.max_relerr(host_rows(norm, rows), exact, fmt) <= compare.TOL[fmt]
+    # and it differs from the fp32-sum reading somewhere (the option is live)
+    _, r_fp32, _ = oracle.ar_rms(P, R, bits(inp["weight"]), wl.eps, True, fmt)
+    assert not compare.bits_equal(r, r_fp32)
+
+
+def test_round_reduced_quant():
+    wl = WORKLOADS["c4"]
+    inp = cuda_inputs(wl, 256)
+    outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"], inp["weight"],
+                                                wl.eps, wl.group, round_reduced=True)
+    torch.cuda.synchronize()
+    norm, q, scales, res = outs
+    P = [bits(p) for p in inp["partials"]]
+    n_o, c_o, s_o, r_o, exact = oracle.ar_rms_quant(P, bits(inp["residual"]), bits(inp["weight"]),
+                                                    wl.eps, False, wl.group, round_reduced=True)
+    assert compare.bits_equal(bits(res), r_o)
+    assert compare.max_relerr(bits(norm), exact, oracle.BF16) <= compare.TOL[oracle.BF16]
+    assert compare.max_code_distance(q.view(torch.uint8).cpu().numpy(), c_o) <= 1
+    assert compare.max_scale_relerr(scales.cpu().numpy(), s_o) <= compare.SCALE_TOL
+
+
+@pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
+def test_round_reduced_worked_case(flags):
+    """P = {1, 2^-8}, R = 2^-9 in bf16: fp32 sum gives 1 + 2^-7, the rounded sum 1."""
+    H = 1024
+    one = torch.ones(2, H, dtype=torch.bfloat16, device=DEV)
+    parts = [one, one * 2.0 ** -8]
+    res = one * 2.0 ** -9
+    w = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+    _, r_fused = arrms.fused_allreduce_rms_norm(parts, res, w, 1e-6, flags=flags)
+    _, r_round = arrms.fused_allreduce_rms_norm(parts, res, w, 1e-6, flags=flags,
+                                                round_reduced=True)
+    torch.cuda.synchronize()
+    assert torch.all(r_fused == 1.0 + 2.0 ** -7)
+    assert torch.all(r_round == 1.0)

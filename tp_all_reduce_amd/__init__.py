@@ -11,7 +11,7 @@ _BINDING_NAMES = (
     "ar_rms_plan", "ar_rms_plan_destroy", "ar_rms_plan_kernel", "ar_rms_one_stage",
     "ar_rms_run", "ar_rms_quant_run", "ar_qknorm_run", "ar_rms_last_error",
     "Plan", "ArrmsError", "OK", "EINVAL", "ENOTSUP", "EHIP", "ENOMEM",
-    "BF16", "FP16", "FORCE_ROW", "FORCE_SPLIT", "KERNEL_ROW", "KERNEL_SPLIT",
+    "BF16", "FP16", "FORCE_ROW", "FORCE_SPLIT", "ROUND_REDUCED", "KERNEL_ROW", "KERNEL_SPLIT",
     "fused_allreduce_rms_norm", "fused_allreduce_rms_norm_quant", "fused_qk_norm",
 )
 

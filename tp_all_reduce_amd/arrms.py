@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(PKG, "libarrms.so")
 
 OK, EINVAL, ENOTSUP, EHIP, ENOMEM = 0, -1, -2, -3, -4
 BF16, FP16 = 0, 1
-FORCE_ROW, FORCE_SPLIT = 1, 2
+FORCE_ROW, FORCE_SPLIT, ROUND_REDUCED = 1, 2, 4
 KERNEL_ROW, KERNEL_SPLIT = 0, 1
 _STATUS = {OK: "OK", EINVAL: "EINVAL", ENOTSUP: "ENOTSUP", EHIP: "EHIP", ENOMEM: "ENOMEM"}
 _TORCH_DTYPE = {BF16: torch.bfloat16, FP16: torch.float16}
@@ -231,10 +231,13 @@ def _tokens(x: torch.Tensor) -> tuple[int, int]:
 
 
 def fused_allreduce_rms_norm(partials, residual, weight, eps: float, gemma: bool = False,
-                             residual_out="new", flags: int = 0, stream=None):
+                             residual_out="new", flags: int = 0, stream=None,
+                             round_reduced: bool = False):
     """Returns (norm_out, residual_out) shaped like the first partial and the
     residual.  residual_out="new" allocates it, None skips it (dead residual),
-    a tensor receives it (may be `residual` itself)."""
+    a tensor receives it (may be `residual` itself).  round_reduced rounds the
+    W-way sum to 16 bits before the residual add (the unfused path's numerics)."""
+    flags |= ROUND_REDUCED if round_reduced else 0
     x = partials[0]
     T, H = _tokens(x)
     dtype = _CODE_OF[x.dtype]
@@ -248,9 +251,11 @@ def fused_allreduce_rms_norm(partials, residual, weight, eps: float, gemma: bool
 
 def fused_allreduce_rms_norm_quant(partials, residual, weight, eps: float, group_size: int = 128,
                                    gemma: bool = False, with_norm: bool = True,
-                                   residual_out="new", flags: int = 0, stream=None):
+                                   residual_out="new", flags: int = 0, stream=None,
+                                   round_reduced: bool = False):
     """Returns (norm_out or None, q_out [.., H] float8_e4m3fn, scales
     [.., H // group_size] fp32, residual_out)."""
+    flags |= ROUND_REDUCED if round_reduced else 0
     x = partials[0]
     T, H = _tokens(x)
     dtype = _CODE_OF[x.dtype]

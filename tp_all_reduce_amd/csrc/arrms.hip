@@ -176,7 +176,7 @@ struct RmsParams {
     int32_t H;
     int32_t packs;                // H / 8
     float eps;
-    int32_t gemma;                // weight applied as 1 + w (Gemma RMSNorm)
+    int32_t options;              // kGemma | kRoundReduced
     int32_t group_lanes;          // group_size / 8
     int32_t groups;               // H / group_size
     int32_t block;                // threads per workgroup (the launch's blockDim.x)
@@ -204,6 +204,10 @@ __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int ti
 // One pack per lane: up to 1024 lanes.  Several packs per lane (rows longer
 // than 1024 packs): up to 512 lanes, which leaves 256 registers per lane.
 constexpr int rms_block_bound(int ppl) { return ppl == 1 ? kMaxBlock : kMaxBlock / 2; }
+
+// Option bits of a reduce+norm call.
+constexpr int32_t kGemma = 1;         // weight applied as 1 + w (Gemma RMSNorm)
+constexpr int32_t kRoundReduced = 2;  // W-way sum rounded to 16 bits before the residual
 
 // Kernel modes.  kRow: one row per workgroup, straight-line code.  kSplit:
 // persistent workgroups looping over rows, the next row's loads issued one row
@@ -280,6 +284,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[k][i] = acc[k][i] + x[i];
             }
+            if (p.options & kRoundReduced) unpack8<IO>(pack8<IO>(acc[k]), acc[k]);
             if constexpr (RES) {
                 float x[8];
                 unpack8<IO>(cur[k][W], x);
@@ -312,7 +317,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
             const bool valid = pk < p.packs;
             float w[8];
             unpack8<IO>(wraw[k], w);
-            if (p.gemma) {
+            if (p.options & kGemma) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) w[i] = w[i] + 1.0f;
             }
@@ -361,12 +366,12 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
 }
 
 // Kernel entry with flat arguments: the first eight (14 dwords: residual,
-// weight, H, gemma and the first four partials) are preloaded into SGPRs at
+// weight, H, options and the first four partials) are preloaded into SGPRs at
 // wave launch (built with kernarg preloading), so a row's loads start without
 // a round trip for their addresses.
 template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
 __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
-    const uint8_t *residual, const uint8_t *weight, int32_t H, int32_t gemma,
+    const uint8_t *residual, const uint8_t *weight, int32_t H, int32_t options,
     const uint8_t *p0, const uint8_t *p1, const uint8_t *p2, const uint8_t *p3,
     const uint8_t *p4, const uint8_t *p5, const uint8_t *p6, const uint8_t *p7,
     uint8_t *norm_out, uint8_t *residual_out, uint8_t *q_out, float *scales, int64_t T,
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
     p.H = H;
     p.packs = H >> 3;
     p.eps = eps;
-    p.gemma = gemma;
+    p.options = options;
     p.group_lanes = group_lanes;
     p.groups = QUANT ? H / (group_lanes * kPackElems) : 0;
     p.block = block;
@@ -570,7 +575,7 @@ hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStre
     RmsParams a = p;
     a.block = int32_t(block);
     a.grid = int32_t(grid);
-    void *args[] = {&a.residual, &a.weight, &a.H, &a.gemma,
+    void *args[] = {&a.residual, &a.weight, &a.H, &a.options,
                     &a.partials[0], &a.partials[1], &a.partials[2], &a.partials[3],
                     &a.partials[4], &a.partials[5], &a.partials[6], &a.partials[7],
                     &a.norm_out, &a.residual_out, &a.q_out, &a.scales, &a.T, &a.eps,
@@ -719,7 +724,7 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
     p.H = int32_t(plan->H);
     p.packs = int32_t(plan->H / kPackElems);
     p.eps = eps;
-    p.gemma = gemma ? 1 : 0;
+    p.options = (gemma ? kGemma : 0) | ((plan->flags & ARRMS_ROUND_REDUCED) ? kRoundReduced : 0);
     p.group_lanes = quant ? group_size / kPackElems : 1;
     p.groups = quant ? int32_t(plan->H / group_size) : 0;
     // The split plan launches min(T, resident workgroups); when every row gets

@@ -182,7 +182,7 @@ extern "C" int ar_rms_plan(int W, int64_t T, int64_t H, int dtype, uint32_t flag
     if (H <= 0) return fail(ARRMS_EINVAL, "H must be > 0 (got %lld)", (long long)H);
     if (dtype != ARRMS_BF16 && dtype != ARRMS_FP16)
         return fail(ARRMS_EINVAL, "unknown dtype %d", dtype);
-    const uint32_t known = ARRMS_FORCE_ROW | ARRMS_FORCE_SPLIT;
+    const uint32_t known = ARRMS_FORCE_ROW | ARRMS_FORCE_SPLIT | ARRMS_ROUND_REDUCED;
     if (flags & ~known) return fail(ARRMS_EINVAL, "unknown flag bits 0x%x", flags & ~known);
     if ((flags & ARRMS_FORCE_ROW) && (flags & ARRMS_FORCE_SPLIT))
         return fail(ARRMS_EINVAL, "FORCE_ROW and FORCE_SPLIT are exclusive");
