@@ -176,7 +176,7 @@ struct RmsParams {
     int32_t H;
     int32_t packs;                // H / 8
     float eps;
-    int32_t options;              // kGemma | kRoundReduced
+    int32_t options;              // kGemma
     int32_t group_lanes;          // group_size / 8
     int32_t groups;               // H / group_size
     int32_t block;                // threads per workgroup (the launch's blockDim.x)
@@ -207,7 +207,6 @@ constexpr int rms_block_bound(int ppl) { return ppl == 1 ? kMaxBlock : kMaxBlock
 
 // Option bits of a reduce+norm call.
 constexpr int32_t kGemma = 1;         // weight applied as 1 + w (Gemma RMSNorm)
-constexpr int32_t kRoundReduced = 2;  // W-way sum rounded to 16 bits before the residual
 
 // Kernel modes.  kRow: one row per workgroup, straight-line code.  kSplit:
 // persistent workgroups looping over rows, the next row's loads issued one row
@@ -216,8 +215,11 @@ constexpr int32_t kRoundReduced = 2;  // W-way sum rounded to 16 bits before the
 enum Mode { kRow = 0, kSplit = 1, kSplitWide = 2 };
 
 // RES: a residual term is present (compile-time, so that every load of a row
-// is issued before the first wait).
-template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
+// is issued before the first wait).  ROUND: the W-way sum is rounded to the
+// I/O format before the residual add, as an all-reduce that writes its result
+// before a separate norm kernel would have it (compile-time: on the latency-
+// bound row path even a select per element costs time).
+template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES, bool ROUND>
 __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     __shared__ float wave_sums[2][kMaxBlock / 64];
     const int tid = threadIdx.x;
@@ -284,7 +286,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[k][i] = acc[k][i] + x[i];
             }
-            if (p.options & kRoundReduced) unpack8<IO>(pack8<IO>(acc[k]), acc[k]);
+            if constexpr (ROUND) unpack8<IO>(pack8<IO>(acc[k]), acc[k]);
             if constexpr (RES) {
                 float x[8];
                 unpack8<IO>(cur[k][W], x);
@@ -369,7 +371,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
 // weight, H, options and the first four partials) are preloaded into SGPRs at
 // wave launch (built with kernarg preloading), so a row's loads start without
 // a round trip for their addresses.
-template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
+template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES, bool ROUND>
 __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
     const uint8_t *residual, const uint8_t *weight, int32_t H, int32_t options,
     const uint8_t *p0, const uint8_t *p1, const uint8_t *p2, const uint8_t *p3,
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
     p.groups = QUANT ? H / (group_lanes * kPackElems) : 0;
     p.block = block;
     p.grid = grid;
-    reduce_norm<IO, W, PPL, MODE, QUANT, RES>(p);
+    reduce_norm<IO, W, PPL, MODE, QUANT, RES, ROUND>(p);
 }
 
 // ------------------------------------------------------------- QK-norm
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(
 using RmsLaunch = hipError_t (*)(const RmsParams &, unsigned, unsigned, hipStream_t);
 using QkLaunch = hipError_t (*)(const QkParams &, unsigned, unsigned, hipStream_t);
 
-template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
+template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES, bool ROUND>
 hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStream_t s) {
     RmsParams a = p;
     a.block = int32_t(block);
@@ -581,7 +583,7 @@ hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStre
                     &a.norm_out, &a.residual_out, &a.q_out, &a.scales, &a.T, &a.eps,
                     &a.group_lanes, &a.block, &a.grid};
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES>),
+        reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES, ROUND>),
         dim3(grid), dim3(block), args, 0, s);
 }
 
@@ -604,48 +606,58 @@ struct Variant {
     const void *symbol;
 };
 
-template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES>
+template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES, bool ROUND>
 Variant variant() {
-    return Variant{&launch_rms<IO, W, PPL, MODE, QUANT, RES>,
-                   reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES>)};
+    return Variant{
+        &launch_rms<IO, W, PPL, MODE, QUANT, RES, ROUND>,
+        reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES, ROUND>)};
 }
 
 // Modes built: kRow and kSplit with one pack per lane, kSplitWide with four
 // packs per lane (rows longer than 8192 elements).
-template <typename IO, int W, bool QUANT, bool RES>
+template <typename IO, int W, bool QUANT, bool RES, bool ROUND>
 Variant pick_mode(int mode) {
     switch (mode) {
-    case kRow: return variant<IO, W, 1, kRow, QUANT, RES>();
-    case kSplit: return variant<IO, W, 1, kSplit, QUANT, RES>();
-    case kSplitWide: return variant<IO, W, kMaxPpl, kSplitWide, QUANT, RES>();
+    case kRow: return variant<IO, W, 1, kRow, QUANT, RES, ROUND>();
+    case kSplit: return variant<IO, W, 1, kSplit, QUANT, RES, ROUND>();
+    case kSplitWide: return variant<IO, W, kMaxPpl, kSplitWide, QUANT, RES, ROUND>();
     default: return Variant{nullptr, nullptr};
     }
 }
 
-template <typename IO, bool QUANT, bool RES>
+// W = 1 has no ROUND variant: a single partial is already in the I/O format,
+// so rounding the "sum" changes nothing.
+template <typename IO, bool QUANT, bool RES, bool ROUND>
 Variant pick_w(int W, int mode) {
     switch (W) {
-    case 1: return pick_mode<IO, 1, QUANT, RES>(mode);
-    case 2: return pick_mode<IO, 2, QUANT, RES>(mode);
-    case 3: return pick_mode<IO, 3, QUANT, RES>(mode);
-    case 4: return pick_mode<IO, 4, QUANT, RES>(mode);
-    case 5: return pick_mode<IO, 5, QUANT, RES>(mode);
-    case 6: return pick_mode<IO, 6, QUANT, RES>(mode);
-    case 7: return pick_mode<IO, 7, QUANT, RES>(mode);
-    case 8: return pick_mode<IO, 8, QUANT, RES>(mode);
+    case 1: return pick_mode<IO, 1, QUANT, RES, false>(mode);
+    case 2: return pick_mode<IO, 2, QUANT, RES, ROUND>(mode);
+    case 3: return pick_mode<IO, 3, QUANT, RES, ROUND>(mode);
+    case 4: return pick_mode<IO, 4, QUANT, RES, ROUND>(mode);
+    case 5: return pick_mode<IO, 5, QUANT, RES, ROUND>(mode);
+    case 6: return pick_mode<IO, 6, QUANT, RES, ROUND>(mode);
+    case 7: return pick_mode<IO, 7, QUANT, RES, ROUND>(mode);
+    case 8: return pick_mode<IO, 8, QUANT, RES, ROUND>(mode);
     default: return Variant{nullptr, nullptr};
     }
+}
+
+template <typename IO, bool ROUND>
+Variant pick_flavour(int W, int mode, bool quant, bool res) {
+    if (quant)
+        return res ? pick_w<IO, true, true, ROUND>(W, mode) : pick_w<IO, true, false, ROUND>(W, mode);
+    return res ? pick_w<IO, false, true, ROUND>(W, mode) : pick_w<IO, false, false, ROUND>(W, mode);
 }
 
 template <typename IO>
-Variant pick_io(int W, int mode, bool quant, bool res) {
-    if (quant) return res ? pick_w<IO, true, true>(W, mode) : pick_w<IO, true, false>(W, mode);
-    return res ? pick_w<IO, false, true>(W, mode) : pick_w<IO, false, false>(W, mode);
+Variant pick_io(int W, int mode, bool quant, bool res, bool round) {
+    return round ? pick_flavour<IO, true>(W, mode, quant, res)
+                 : pick_flavour<IO, false>(W, mode, quant, res);
 }
 
-Variant pick_rms(int dtype, int W, int mode, bool quant, bool res) {
-    return dtype == ARRMS_BF16 ? pick_io<Bf16>(W, mode, quant, res)
-                               : pick_io<Fp16>(W, mode, quant, res);
+Variant pick_rms(int dtype, int W, int mode, bool quant, bool res, bool round) {
+    return dtype == ARRMS_BF16 ? pick_io<Bf16>(W, mode, quant, res, round)
+                               : pick_io<Fp16>(W, mode, quant, res, round);
 }
 
 template <typename IO, int W, bool LOOP>
@@ -724,7 +736,7 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
     p.H = int32_t(plan->H);
     p.packs = int32_t(plan->H / kPackElems);
     p.eps = eps;
-    p.options = (gemma ? kGemma : 0) | ((plan->flags & ARRMS_ROUND_REDUCED) ? kRoundReduced : 0);
+    p.options = gemma ? kGemma : 0;
     p.group_lanes = quant ? group_size / kPackElems : 1;
     p.groups = quant ? int32_t(plan->H / group_size) : 0;
     // The split plan launches min(T, resident workgroups); when every row gets
@@ -733,7 +745,8 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
     const bool split = plan->kernel == ARRMS_KERNEL_SPLIT;
     int mode = !split ? kRow : (plan->ppl == 1 ? kSplit : kSplitWide);
     const bool res = residual != nullptr;
-    Variant v = pick_rms(plan->dtype, plan->W, mode, quant, res);
+    const bool round = (plan->flags & ARRMS_ROUND_REDUCED) != 0;
+    Variant v = pick_rms(plan->dtype, plan->W, mode, quant, res, round);
     if (v.launch == nullptr)
         return fail(ARRMS_ENOTSUP, "no kernel for W=%d, %d packs per lane", plan->W, plan->ppl);
     int64_t grid = plan->T;
@@ -744,7 +757,7 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
             grid = resident;
         } else if (mode == kSplit) {
             mode = kRow;
-            v = pick_rms(plan->dtype, plan->W, mode, quant, res);
+            v = pick_rms(plan->dtype, plan->W, mode, quant, res, round);
         }
     }
     hipError_t e = v.launch(p, unsigned(grid), unsigned(plan->block), static_cast<hipStream_t>(stream));
