@@ -85,11 +85,13 @@ int ar_rms_one_stage(int W, int64_t T, int64_t H, int dtype, int fully_connected
  * Builds a plan for W partial buffers of [T, H] in format `dtype`.  The kernel
  * is the row-resident one when ar_rms_one_stage(W, T, H, dtype, 1) holds (an
  * MI355X xGMI group is fully connected) and the split one otherwise, unless a
- * FORCE flag says which.
+ * FORCE flag says which.  W may exceed the pages' eight ranks (up to 16, for
+ * rows of at most 8192 elements); such plans always use the split kernel.
  * Errors: EINVAL for out == NULL, W < 1, T < 0, H <= 0, unknown dtype, unknown
- * flag bits or both FORCE flags; ENOTSUP for W > 8, H % 8 != 0, H > 16384, or
- * FORCE_ROW with T > 80 or H/8 > 1024; ENOMEM.  On success *out owns a host
- * allocation released by ar_rms_plan_destroy.
+ * flag bits or both FORCE flags; ENOTSUP for W > 16, W > 8 with H > 8192,
+ * H % 8 != 0, H > 16384, or FORCE_ROW with W > 8, T > 80 or H/8 > 1024;
+ * ENOMEM.  On success *out owns a host allocation released by
+ * ar_rms_plan_destroy.
  */
 int ar_rms_plan(int W, int64_t T, int64_t H, int dtype, uint32_t flags, ar_rms_plan_t *out);
 
@@ -162,7 +164,8 @@ int ar_rms_quant_run(const ar_rms_plan_s *plan, const void *const *partials,
  * ENOTSUP unless q_size and kv_size are positive multiples of 256 (32 lanes of
  * 16-byte packs: the alignment the fused QK kernel requires, PR #44849 page,
  * "Implementation breakdown" item 3) with q_size + 2 * kv_size == H and
- * W * (q_size + kv_size) <= 32768; the plan's FORCE flags do not apply.
+ * W * (q_size + kv_size) <= 32768, and unless W <= 8; the plan's FORCE flags
+ * do not apply.
  */
 int ar_qknorm_run(const ar_rms_plan_s *plan, const void *const *qkv, int q_size, int kv_size,
                   const void *q_weight, const void *k_weight, float eps, void *q_out,

@@ -80,7 +80,9 @@ def test_plan_dispatch_for_the_workloads():
     ((2, 8, 1024, 2, 0), arrms.EINVAL),          # fp32 / unknown dtype
     ((2, 8, 1024, 0, 8), arrms.EINVAL),          # unknown flag bit
     ((2, 8, 1024, 0, 3), arrms.EINVAL),          # both FORCE flags
-    ((9, 8, 1024, 0, 0), arrms.ENOTSUP),         # W > 8
+    ((17, 8, 1024, 0, 0), arrms.ENOTSUP),        # W > 16
+    ((9, 8, 8200, 0, 0), arrms.ENOTSUP),         # W > 8 with rows beyond 8192
+    ((9, 8, 1024, 0, 1), arrms.ENOTSUP),         # FORCE_ROW with W > 8
     ((2, 8, 1020, 0, 0), arrms.ENOTSUP),         # H % 8 != 0
     ((2, 8, 16392, 0, 0), arrms.ENOTSUP),        # H > 16384
     ((2, 81, 1024, 0, 1), arrms.ENOTSUP),        # FORCE_ROW beyond 80 tokens
@@ -90,6 +92,14 @@ def test_plan_errors(args, code):
     with pytest.raises(arrms.ArrmsError) as e:
         arrms.ar_rms_plan(*args)
     assert e.value.code == code and e.value.message
+
+
+def test_more_than_eight_partials_plan_the_split_kernel():
+    for W in (9, 12, 16):
+        for flags in (0, arrms.FORCE_SPLIT):
+            p = arrms.ar_rms_plan(W, 8, 8192, 0, flags)
+            assert p.kernel == arrms.KERNEL_SPLIT
+        assert not arrms.ar_rms_one_stage(W, 8, 1024)
 
 
 def test_round_reduced_flag_accepted_with_any_kernel():
@@ -197,6 +207,8 @@ def test_qk_validation():
     assert _qk(plan, 1024, 256) == arrms.ENOTSUP          # q + 2 kv != H
     big = arrms.ar_rms_plan(8, 64, 4096 + 2 * 1024)
     assert _qk(big, 4096, 1024) == arrms.ENOTSUP          # W (q + kv) > 32768
+    many = arrms.ar_rms_plan(9, 64, 768)
+    assert _qk(many, 256, 256) == arrms.ENOTSUP           # more than eight shards
     zero = arrms.ar_rms_plan(4, 0, 2048)
     assert _qk(zero, 1536, 256) == arrms.OK
 

@@ -56,12 +56,15 @@ def run_rms(inp, eps, gemma, flags=0, residual_out="new"):
                                           gemma, residual_out=residual_out, flags=flags)
 
 
+def to_cuda(inp):
+    return {k: ([x.to(DEV) for x in v] if isinstance(v, list) else v.to(DEV))
+            for k, v in inp.items()}
+
+
 def cuda_inputs(wl, T, dtype=torch.bfloat16, device_draw=False, **kw):
     if device_draw:
         return workloads.make_inputs(wl, T, dtype, device=DEV, **kw)
-    inp = workloads.make_inputs(wl, T, dtype, device="cpu", **kw)
-    return {k: ([x.to(DEV) for x in v] if isinstance(v, list) else v.to(DEV))
-            for k, v in inp.items()}
+    return to_cuda(workloads.make_inputs(wl, T, dtype, device="cpu", **kw))
 
 
 # ------------------------------------------------------------ the workloads
@@ -143,6 +146,37 @@ def test_c5_qk_norm():
                                        wl.q_size, wl.kv_size, wl.eps)
     torch.cuda.synchronize()
     check_qk(inp, wl.q_size, wl.kv_size, wl.eps, q_out, k_out)
+
+
+FP16_CASES = ([("c1", 8)] + [("c2", T) for T in WORKLOADS["c2"].Ts]
+              + [("c3", T) for T in WORKLOADS["c3"].Ts] + [("c4", 256)])
+
+
+@pytest.mark.parametrize("name,T", FP16_CASES, ids=[f"{n}_T{T}" for n, T in FP16_CASES])
+def test_workloads_fp16(name, T):
+    """Every reduce+norm workload again with fp16 activations and weight."""
+    wl = WORKLOADS[name]
+    inp = cuda_inputs(wl, T, torch.float16, device_draw=name == "c3")
+    rows = np.arange(T) if T <= 1024 else sample_rows(T, 256, seed=T)
+    if wl.group:
+        outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"],
+                                                    inp["weight"], wl.eps, wl.group, wl.gemma)
+        torch.cuda.synchronize()
+        assert check_quant(inp, wl.eps, wl.gemma, wl.group, outs, fmt=oracle.FP16) < 0.01
+    else:
+        flags = arrms.FORCE_ROW if name == "c2" else 0
+        norm, res = run_rms(inp, wl.eps, wl.gemma, flags=flags)
+        torch.cuda.synchronize()
+        check_rms(inp, norm, res, wl.eps, wl.gemma, rows=rows, fmt=oracle.FP16)
+
+
+def test_c5_qk_norm_fp16():
+    wl = WORKLOADS["c5"]
+    inp = to_cuda(workloads.make_qk_inputs(wl, 64, torch.float16))
+    q_out, k_out = arrms.fused_qk_norm(inp["shards"], inp["q_weight"], inp["k_weight"],
+                                       wl.q_size, wl.kv_size, wl.eps)
+    torch.cuda.synchronize()
+    check_qk(inp, wl.q_size, wl.kv_size, wl.eps, q_out, k_out, fmt=oracle.FP16)
 
 
 # ------------------------------------------------- shapes: tiles and tails
@@ -385,6 +419,51 @@ def test_split_loops_over_rows(W, T, H, quant):
         norm, res = run_rms(inp, 1e-6, False, flags=arrms.FORCE_SPLIT)
         torch.cuda.synchronize()
         check_rms(inp, norm, res, 1e-6, False, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("W,T,H", [(9, 1, 8), (11, 5, 72), (12, 37, 1000), (16, 300, 8192),
+                                   (16, 3000, 4096), (13, 2000, 1096)])
+def test_more_than_eight_partials(W, T, H, dtype):
+    """W = 9..16: the persistent body without prefetch; T = 2000 and 3000 loop."""
+    inp = cuda_inputs(GENERIC, T, dtype, W=W, H=H, seed=W * 131 + T + H, device_draw=T > 1000)
+    norm, res = run_rms(inp, 1e-5, False)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 300 else sample_rows(T, 160, seed=W)
+    check_rms(inp, norm, res, 1e-5, False, rows=rows, fmt=FMT[dtype])
+
+
+@pytest.mark.parametrize("variant", ["quant", "quant_gemma_no_norm", "round", "no_residual",
+                                     "dead_residual"])
+def test_more_than_eight_partials_variants(variant):
+    W, T, H = 16, 100, 7168
+    inp = cuda_inputs(GENERIC, T, W=W, H=H, seed=len(variant))
+    if variant.startswith("quant"):
+        gemma = "gemma" in variant
+        outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"],
+                                                    inp["weight"], 1e-6, 128, gemma,
+                                                    with_norm="no_norm" not in variant)
+        torch.cuda.synchronize()
+        assert check_quant(inp, 1e-6, gemma, 128, outs) < 0.01
+    elif variant == "round":
+        norm, res = arrms.fused_allreduce_rms_norm(inp["partials"], inp["residual"],
+                                                   inp["weight"], 1e-6, round_reduced=True)
+        torch.cuda.synchronize()
+        P = [bits(p) for p in inp["partials"]]
+        _, r, exact = oracle.ar_rms(P, bits(inp["residual"]), bits(inp["weight"]), 1e-6, False,
+                                    round_reduced=True)
+        assert compare.bits_equal(bits(res), r)
+        assert compare.max_relerr(bits(norm), exact, oracle.BF16) <= compare.TOL[oracle.BF16]
+    elif variant == "no_residual":
+        inp["residual"] = None
+        norm, res = run_rms(inp, 1e-6, False)
+        torch.cuda.synchronize()
+        check_rms(inp, norm, res, 1e-6, False)
+    else:
+        norm, res = run_rms(inp, 1e-6, False, residual_out=None)
+        torch.cuda.synchronize()
+        assert res is None
+        check_rms(inp, norm, None, 1e-6, False, expect_residual=False)
 
 
 def test_qk_more_tokens_than_workgroups():

@@ -210,8 +210,10 @@ constexpr int32_t kGemma = 1;         // weight applied as 1 + w (Gemma RMSNorm)
 
 // Kernel modes.  kRow: one row per workgroup, straight-line code.  kSplit:
 // persistent workgroups looping over rows, the next row's loads issued one row
-// ahead.  kSplitWide: persistent, several packs per lane, loads at the top of
-// each row (no room in registers for a second row).
+// ahead.  kSplitWide: persistent, loads at the top of each row, for shapes that
+// leave no room in registers for a second row: four packs per lane (rows
+// longer than 8192 elements), or one pack per lane with more than eight
+// partials.
 enum Mode { kRow = 0, kSplit = 1, kSplitWide = 2 };
 
 // RES: a residual term is present (compile-time, so that every load of a row
@@ -377,10 +379,14 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
     const uint8_t *p0, const uint8_t *p1, const uint8_t *p2, const uint8_t *p3,
     const uint8_t *p4, const uint8_t *p5, const uint8_t *p6, const uint8_t *p7,
     uint8_t *norm_out, uint8_t *residual_out, uint8_t *q_out, float *scales, int64_t T,
-    float eps, int32_t group_lanes, int32_t block, int32_t grid) {
+    float eps, int32_t group_lanes, int32_t block, int32_t grid,
+    const uint8_t *p8, const uint8_t *p9, const uint8_t *p10, const uint8_t *p11,
+    const uint8_t *p12, const uint8_t *p13, const uint8_t *p14, const uint8_t *p15) {
     RmsParams p;
     p.partials[0] = p0; p.partials[1] = p1; p.partials[2] = p2; p.partials[3] = p3;
     p.partials[4] = p4; p.partials[5] = p5; p.partials[6] = p6; p.partials[7] = p7;
+    p.partials[8] = p8; p.partials[9] = p9; p.partials[10] = p10; p.partials[11] = p11;
+    p.partials[12] = p12; p.partials[13] = p13; p.partials[14] = p14; p.partials[15] = p15;
     p.residual = residual;
     p.weight = weight;
     p.norm_out = norm_out;
@@ -428,8 +434,8 @@ struct Shards {
     const uint8_t *x0, *x1, *x2, *x3, *x4, *x5, *x6, *x7;
     template <int W>
     __device__ __forceinline__ const uint8_t *pick(int r) const {
-        const uintptr_t a[kMaxW] = {uintptr_t(x0), uintptr_t(x1), uintptr_t(x2), uintptr_t(x3),
-                                    uintptr_t(x4), uintptr_t(x5), uintptr_t(x6), uintptr_t(x7)};
+        const uintptr_t a[kMaxQkW] = {uintptr_t(x0), uintptr_t(x1), uintptr_t(x2), uintptr_t(x3),
+                                      uintptr_t(x4), uintptr_t(x5), uintptr_t(x6), uintptr_t(x7)};
         uintptr_t q = a[0];
 #pragma unroll
         for (int i = 1; i < W; ++i) q = r == i ? a[i] : q;
@@ -581,7 +587,9 @@ hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStre
                     &a.partials[0], &a.partials[1], &a.partials[2], &a.partials[3],
                     &a.partials[4], &a.partials[5], &a.partials[6], &a.partials[7],
                     &a.norm_out, &a.residual_out, &a.q_out, &a.scales, &a.T, &a.eps,
-                    &a.group_lanes, &a.block, &a.grid};
+                    &a.group_lanes, &a.block, &a.grid,
+                    &a.partials[8], &a.partials[9], &a.partials[10], &a.partials[11],
+                    &a.partials[12], &a.partials[13], &a.partials[14], &a.partials[15]};
     return hipLaunchKernel(
         reinterpret_cast<const void *>(&reduce_norm_kernel<IO, W, PPL, MODE, QUANT, RES, ROUND>),
         dim3(grid), dim3(block), args, 0, s);
@@ -625,6 +633,14 @@ Variant pick_mode(int mode) {
     }
 }
 
+// More than eight partials: only the persistent body without prefetch, one
+// pack per lane (the plan limits such rows to 8192 elements).
+template <typename IO, int W, bool QUANT, bool RES, bool ROUND>
+Variant pick_mode_many(int mode) {
+    if (mode != kSplitWide) return Variant{nullptr, nullptr};
+    return variant<IO, W, 1, kSplitWide, QUANT, RES, ROUND>();
+}
+
 // W = 1 has no ROUND variant: a single partial is already in the I/O format,
 // so rounding the "sum" changes nothing.
 template <typename IO, bool QUANT, bool RES, bool ROUND>
@@ -638,6 +654,14 @@ Variant pick_w(int W, int mode) {
     case 6: return pick_mode<IO, 6, QUANT, RES, ROUND>(mode);
     case 7: return pick_mode<IO, 7, QUANT, RES, ROUND>(mode);
     case 8: return pick_mode<IO, 8, QUANT, RES, ROUND>(mode);
+    case 9: return pick_mode_many<IO, 9, QUANT, RES, ROUND>(mode);
+    case 10: return pick_mode_many<IO, 10, QUANT, RES, ROUND>(mode);
+    case 11: return pick_mode_many<IO, 11, QUANT, RES, ROUND>(mode);
+    case 12: return pick_mode_many<IO, 12, QUANT, RES, ROUND>(mode);
+    case 13: return pick_mode_many<IO, 13, QUANT, RES, ROUND>(mode);
+    case 14: return pick_mode_many<IO, 14, QUANT, RES, ROUND>(mode);
+    case 15: return pick_mode_many<IO, 15, QUANT, RES, ROUND>(mode);
+    case 16: return pick_mode_many<IO, 16, QUANT, RES, ROUND>(mode);
     default: return Variant{nullptr, nullptr};
     }
 }
@@ -743,7 +767,8 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
     // its own workgroup the straight-line row body is used (the loop costs
     // latency and has nothing to overlap).
     const bool split = plan->kernel == ARRMS_KERNEL_SPLIT;
-    int mode = !split ? kRow : (plan->ppl == 1 ? kSplit : kSplitWide);
+    int mode = !split ? kRow
+                      : (plan->ppl == 1 && plan->W <= kMaxPrefetchW ? kSplit : kSplitWide);
     const bool res = residual != nullptr;
     const bool round = (plan->flags & ARRMS_ROUND_REDUCED) != 0;
     Variant v = pick_rms(plan->dtype, plan->W, mode, quant, res, round);

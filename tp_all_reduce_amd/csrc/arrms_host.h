@@ -20,7 +20,9 @@ struct ar_rms_plan_s {
 
 namespace arrms {
 
-constexpr int kMaxW = 8;            // partial buffers per call
+constexpr int kMaxW = 16;           // partial buffers per reduce+norm call
+constexpr int kMaxPrefetchW = 8;    // beyond: no row-ahead prefetch, rows of at most 8192
+constexpr int kMaxQkW = 8;          // shards per QK-norm call
 constexpr int kPackElems = 8;       // 16-byte pack of 16-bit elements
 constexpr int kMaxBlock = 1024;     // threads per workgroup
 constexpr int kMaxPpl = 4;          // packs per lane of the reduce+norm kernel (rows > 8192)

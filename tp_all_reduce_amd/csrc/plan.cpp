@@ -127,6 +127,9 @@ int check_qk_args(const ar_rms_plan_s *plan, const void *const *qkv, int q_size,
     if (q_size <= 0 || kv_size <= 0)
         return fail(ARRMS_EINVAL, "q_size and kv_size must be positive (got %d, %d)", q_size,
                     kv_size);
+    if (plan->W > kMaxQkW)
+        return fail(ARRMS_ENOTSUP, "QK-norm takes at most %d shards (got W=%d)", kMaxQkW,
+                    plan->W);
     // 32 lanes x one 16-byte pack of 8 elements
     const int align = 32 * kPackElems;
     if (q_size % align != 0 || kv_size % align != 0)
@@ -187,6 +190,9 @@ extern "C" int ar_rms_plan(int W, int64_t T, int64_t H, int dtype, uint32_t flag
     if ((flags & ARRMS_FORCE_ROW) && (flags & ARRMS_FORCE_SPLIT))
         return fail(ARRMS_EINVAL, "FORCE_ROW and FORCE_SPLIT are exclusive");
     if (W > kMaxW) return fail(ARRMS_ENOTSUP, "W=%d exceeds %d partial buffers", W, kMaxW);
+    if (W > kMaxPrefetchW && H / kPackElems > kMaxBlock)
+        return fail(ARRMS_ENOTSUP, "W=%d > %d needs H <= %d (got H=%lld)", W, kMaxPrefetchW,
+                    kMaxBlock * kPackElems, (long long)H);
     if (H % kPackElems != 0)
         return fail(ARRMS_ENOTSUP, "H=%lld is not a multiple of %d (16-byte packs)",
                     (long long)H, kPackElems);
@@ -194,6 +200,8 @@ extern "C" int ar_rms_plan(int W, int64_t T, int64_t H, int dtype, uint32_t flag
                                (long long)kMaxH);
     int kernel;
     if (flags & ARRMS_FORCE_ROW) {
+        if (W > kMaxPrefetchW)
+            return fail(ARRMS_ENOTSUP, "FORCE_ROW needs W <= %d (got W=%d)", kMaxPrefetchW, W);
         if (T > kMaxRowTokens || H / kPackElems > 1024)
             return fail(ARRMS_ENOTSUP,
                         "FORCE_ROW needs T <= 80 and H/8 <= 1024 (got T=%lld, H=%lld)",
