@@ -58,12 +58,26 @@ def e4m3_ord(codes) -> np.ndarray:
     return np.where(c & 0x80, -mag, mag)
 
 
+def e4m3_is_nan(codes) -> np.ndarray:
+    """E4M3FN has two NaN patterns, S.1111.111, whatever the sign bit."""
+    return (np.asarray(codes, np.int32) & 0x7F) == 0x7F
+
+
 def max_code_distance(a, b) -> int:
+    """Largest distance in steps between E4M3FN codes (sign-magnitude order,
+    +0 and -0 equal).  The two NaN patterns are equal to each other; a NaN
+    against a number is an unbounded mismatch."""
     a = np.asarray(a, np.uint8)
     b = np.asarray(b, np.uint8)
     if a.size == 0:
         return 0
-    return int(np.max(np.abs(e4m3_ord(a) - e4m3_ord(b))))
+    na, nb = e4m3_is_nan(a), e4m3_is_nan(b)
+    if not np.array_equal(na, nb):
+        return 1 << 30
+    ok = ~na
+    if not ok.any():
+        return 0
+    return int(np.max(np.abs(e4m3_ord(a[ok]) - e4m3_ord(b[ok]))))
 
 
 def max_scale_relerr(a, b) -> float:

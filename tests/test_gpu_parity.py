@@ -335,6 +335,30 @@ def test_special_values():
         check_rms(inp, norm, res, eps, False, rows=np.array(sel))
 
 
+@pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
+def test_quant_special_values(flags):
+    """FP8 epilogue on non-finite rows: a NaN weight element gives a NaN code in
+    every row while the other groups keep their scales; a row with an inf (norm
+    NaN there, 0 elsewhere), a row with a NaN input (norm NaN everywhere) and a
+    zero row all get scale 0 and code 0, as the oracle's NaN-free amax gives."""
+    W, T, H = 2, 6, 1024
+    inp = cuda_inputs(GENERIC, T, W=W, H=H, seed=321)
+    inp["weight"][5] = float("nan")
+    inp["partials"][0][1, 7] = float("inf")
+    inp["partials"][0][2, 9] = float("nan")
+    for x in (inp["partials"][0], inp["partials"][1], inp["residual"]):
+        x[3].zero_()
+    outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"], inp["weight"],
+                                                1e-6, 128, flags=flags)
+    torch.cuda.synchronize()
+    check_quant(inp, 1e-6, False, 128, outs)
+    q = outs[1].view(torch.uint8).cpu().numpy()
+    scales = outs[2].cpu().numpy()
+    assert (q[[0, 4, 5], 5] & 0x7F == 0x7F).all()      # NaN codes
+    assert (scales[[1, 2, 3]] == 0).all() and (q[[1, 2, 3]] == 0).all()
+    assert (scales[[0, 4, 5]] > 0).all()
+
+
 def test_deterministic_and_row_split_agree():
     wl = WORKLOADS["c2"]
     inp = cuda_inputs(wl, 64)
