@@ -22,8 +22,9 @@ CXX = os.environ.get("CXX_HOST") or shutil.which("g++") or "c++"
 
 # Packed-fp32 VALU ops are disabled for every HIP unit; hipcc's host pass warns
 # that it does not know the feature, which is harmless.
-# Kernel arguments: the first eight of every kernel are preloaded into SGPRs at
-# wave launch (the code object keeps a loading prologue for firmware without it).
+# Kernel arguments: the first eight of every kernel (at most 14 dwords) are
+# preloaded into SGPRs at wave launch (the code object keeps a loading prologue
+# for firmware without it).
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-mllvm", "-amdgpu-kernarg-preload-count=8",

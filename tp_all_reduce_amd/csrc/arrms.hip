@@ -142,6 +142,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// Sum of the first n (<= 16) per-wavefront partials in LDS, the same bits in
+// every lane.  Beyond eight: lane i reads partial i mod 16 (0 from n on) and
+// the 16-lane DPP sum adds them in a fixed tree order, one LDS read and one
+// wait where a loop would read and wait per group of partials.
+__device__ __forceinline__ float sum_wave_partials(const float *ws, int n, int lane) {
+    if (n <= 8) {
+        // few partials: broadcast reads in index order cost less than the DPP
+        float t = 0.0f;
+        for (int i = 0; i < n; ++i) t += ws[i];
+        return t;
+    }
+    const int i = lane & 15;
+    return row16_sum(i < n ? ws[i] : 0.0f);
+}
+
 // Max over aligned groups of `lanes` consecutive lanes (1..64, a power of two);
 // every lane of a group ends with the group's max.
 __device__ __forceinline__ float group_max(float v, int lanes) {
@@ -179,12 +194,22 @@ struct RmsParams {
     int32_t options;              // kGemma
     int32_t group_lanes;          // group_size / 8
     int32_t groups;               // H / group_size
-    int32_t block;                // threads per workgroup (the launch's blockDim.x)
     int32_t grid;                 // workgroups (the launch's gridDim.x)
 };
 
+// Lanes of a workgroup that covers `packs` 16-byte packs with `ppl` packs per
+// lane, in whole wavefronts.  The kernels derive their width from it (reading
+// blockDim goes through the dispatch packet in memory) and the launchers check
+// that the launch agrees.
+__host__ __device__ constexpr int lanes_for(int packs, int ppl) {
+    return ((packs + ppl - 1) / ppl + 63) / 64 * 64;
+}
+
 // Issues the loads of one row: W partial packs and (RES) the residual pack for
-// each of the lane's PPL packs (pack pk = lane + k * workgroup size).
+// each of the lane's PPL packs (pack pk = lane + k * workgroup size).  A lane
+// past the row's end loads pack 0 of the row instead (its sum is zeroed and
+// nothing of it is stored): with no branch around a load, the compiler places
+// no wait at a join.
 template <int W, int PPL, bool RES>
 __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int tid, int nthr,
                                          u32x4 (&v)[PPL][W + RES]) {
@@ -192,13 +217,14 @@ __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int ti
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
         const int pk = tid + k * nthr;
-        if (pk < p.packs) {
-            const size_t off = base + size_t(pk) * 16;
+        const size_t off = base + size_t(pk < p.packs ? pk : 0) * 16;
 #pragma unroll
-            for (int r = 0; r < W; ++r) v[k][r] = load16_stream(p.partials[r] + off);
-            if constexpr (RES) v[k][W] = load16_stream(p.residual + off);
-        }
+        for (int r = 0; r < W; ++r) v[k][r] = load16_stream(p.partials[r] + off);
+        if constexpr (RES) v[k][W] = load16_stream(p.residual + off);
     }
+    // Keep every load ahead of what follows: the scheduler would otherwise put
+    // one behind the wait for the scalar load of the output pointers.
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // One pack per lane: up to 1024 lanes.  Several packs per lane (rows longer
@@ -225,9 +251,9 @@ template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES, bool ROUN
 __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     __shared__ float wave_sums[2][kMaxBlock / 64];
     const int tid = threadIdx.x;
-    // launch shape from the arguments: reading blockDim/gridDim goes through
-    // the dispatch packet in memory
-    const int nthr = p.block;
+    // launch shape from the arguments and the row length (not from
+    // blockDim/gridDim, which go through the dispatch packet in memory)
+    const int nthr = lanes_for(p.packs, PPL);
     const int nwaves = nthr >> 6;
     const int64_t stride = p.grid;
     int64_t row = blockIdx.x;    // < T: the launcher never starts more workgroups than rows
@@ -235,13 +261,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     constexpr int NB = W + RES;      // packs loaded per lane pack: partials, residual
     // kSplit: `ahead` receives the next row's loads one row in advance
     u32x4 ahead[PPL][NB];
-    if constexpr (MODE == kSplit) {
-#pragma unroll
-        for (int k = 0; k < PPL; ++k)
-#pragma unroll
-            for (int r = 0; r < NB; ++r) ahead[k][r] = u32x4{0u, 0u, 0u, 0u};
-        load_row<W, PPL, RES>(p, row, tid, nthr, ahead);
-    }
+    if constexpr (MODE == kSplit) load_row<W, PPL, RES>(p, row, tid, nthr, ahead);
     // weight row: loaded once per workgroup and kept (kSplitWide reloads it
     // per row from L2 after the row's reduction, to stay within registers);
     // converted where used, so no wait on it stands before the row's loads
@@ -250,7 +270,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
             const int pk = tid + k * nthr;
-            wraw[k] = pk < p.packs ? load16(p.weight + size_t(pk) * 16) : u32x4{0u, 0u, 0u, 0u};
+            wraw[k] = load16(p.weight + size_t(pk < p.packs ? pk : 0) * 16);
         }
     };
     if constexpr (MODE != kSplitWide) load_weight();
@@ -266,10 +286,6 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
                 for (int r = 0; r < NB; ++r) cur[k][r] = ahead[k][r];
             if (next < p.T) load_row<W, PPL, RES>(p, next, tid, nthr, ahead);
         } else {
-#pragma unroll
-            for (int k = 0; k < PPL; ++k)
-#pragma unroll
-                for (int r = 0; r < NB; ++r) cur[k][r] = u32x4{0u, 0u, 0u, 0u};
             load_row<W, PPL, RES>(p, row, tid, nthr, cur);
         }
         const size_t base = size_t(row) * size_t(p.H) * 2;
@@ -310,7 +326,12 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
         if ((tid & 63) == 0) wave_sums[parity][tid >> 6] = wsum;
         __syncthreads();
         float total = 0.0f;
-        for (int i = 0; i < nwaves; ++i) total += wave_sums[parity][i];
+        if constexpr (PPL == 1) {
+            total = sum_wave_partials(wave_sums[parity], nwaves, tid);
+        } else {
+            // rows of several packs per lane have registers for nothing more
+            for (int i = 0; i < nwaves; ++i) total += wave_sums[parity][i];
+        }
         const float rstd = rsqrtf(total / float(p.H) + p.eps);
 
         // phase 2: normalise, weight, store; optional FP8 group epilogue
@@ -379,7 +400,7 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
     const uint8_t *p0, const uint8_t *p1, const uint8_t *p2, const uint8_t *p3,
     const uint8_t *p4, const uint8_t *p5, const uint8_t *p6, const uint8_t *p7,
     uint8_t *norm_out, uint8_t *residual_out, uint8_t *q_out, float *scales, int64_t T,
-    float eps, int32_t group_lanes, int32_t block, int32_t grid,
+    float eps, int32_t group_lanes, int32_t grid,
     const uint8_t *p8, const uint8_t *p9, const uint8_t *p10, const uint8_t *p11,
     const uint8_t *p12, const uint8_t *p13, const uint8_t *p14, const uint8_t *p15) {
     RmsParams p;
@@ -400,7 +421,6 @@ __global__ __launch_bounds__(rms_block_bound(PPL)) void reduce_norm_kernel(
     p.options = options;
     p.group_lanes = group_lanes;
     p.groups = QUANT ? H / (group_lanes * kPackElems) : 0;
-    p.block = block;
     p.grid = grid;
     reduce_norm<IO, W, PPL, MODE, QUANT, RES, ROUND>(p);
 }
@@ -415,12 +435,9 @@ struct QkParams {
     uint8_t *q_out;
     uint8_t *k_out;
     int64_t T;
-    int32_t W;
     int32_t q_packs;              // q_size / 8
     int32_t kv_packs;             // kv_size / 8
-    int32_t row_bytes;            // (q_size + 2 kv_size) * 2
     float eps;
-    int32_t block;                // threads per workgroup (the launch's blockDim.x)
     int32_t grid;                 // workgroups (the launch's gridDim.x)
 };
 
@@ -449,24 +466,26 @@ template <typename IO, int W, int PPL, bool LOOP>
 __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     __shared__ float wave_sums[2][2][kMaxBlock / 64];
     const int tid = threadIdx.x;
-    const int nthr = p.block;     // launch shape from the arguments (see reduce_norm)
-    const int nwaves = nthr >> 6;
     const int nq = W * p.q_packs;
     const int n = nq + W * p.kv_packs;
+    const int nthr = lanes_for(n, PPL);   // launch width (see reduce_norm)
+    const int nwaves = nthr >> 6;
+    const size_t row_bytes = size_t(p.q_packs + 2 * p.kv_packs) * 16;
     const int q_size = p.q_packs * 8;
     const int kv_size = p.kv_packs * 8;
 
     // Row-independent lane layout, worked out once: shard r (by comparisons,
     // no integer division), the pack's column in the shard row, the weight
-    // pack, and the output row offset.
+    // pack, and the output row offset.  A lane past the end takes pack 0's
+    // layout (every address in bounds) and is masked by `valid`.
     bool valid[PPL], is_q[PPL];
     const uint8_t *src[PPL];
     int col[PPL], widx[PPL];
     size_t out_off[PPL];
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
-        const int pk = tid + k * nthr;
-        valid[k] = pk < n;
+        valid[k] = tid + k * nthr < n;
+        const int pk = valid[k] ? tid + k * nthr : 0;
         is_q[k] = pk < nq;
         const int idx = is_q[k] ? pk : pk - nq;
         const int per = is_q[k] ? p.q_packs : p.kv_packs;
@@ -482,18 +501,16 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     }
 
     int64_t row = blockIdx.x;     // < T: the launcher never starts more workgroups than rows
+    // Every lane loads (lanes past the end at the clamped pack 0 of shard 0,
+    // then zeroed): with no branch around a load, no wait is placed at a join.
     u32x4 xr[PPL], wr[PPL];
 #pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-        xr[k] = u32x4{0u, 0u, 0u, 0u};
-        if (valid[k]) xr[k] = load16_stream(src[k] + size_t(row) * p.row_bytes + size_t(col[k]) * 16);
-    }
+    for (int k = 0; k < PPL; ++k)
+        xr[k] = load16_stream(src[k] + size_t(row) * row_bytes + size_t(col[k]) * 16);
     // weights: loaded once (the same for every token), after the first loads
 #pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-        wr[k] = u32x4{0u, 0u, 0u, 0u};
-        if (valid[k]) wr[k] = load16((is_q[k] ? p.q_weight : p.k_weight) + size_t(widx[k]) * 16);
-    }
+    for (int k = 0; k < PPL; ++k)
+        wr[k] = load16((is_q[k] ? p.q_weight : p.k_weight) + size_t(widx[k]) * 16);
 
     int parity = 0;
     for (;;) {
@@ -501,6 +518,7 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
         float ssq = 0.0f, ssk = 0.0f;
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
+            if (!valid[k]) xr[k] = u32x4{0u, 0u, 0u, 0u};
             unpack8<IO>(xr[k], x[k]);
             float s = 0.0f;
 #pragma unroll
@@ -511,7 +529,7 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
         if (LOOP && next < p.T) {
 #pragma unroll
             for (int k = 0; k < PPL; ++k)
-                if (valid[k]) xr[k] = load16_stream(src[k] + size_t(next) * p.row_bytes + size_t(col[k]) * 16);
+                xr[k] = load16_stream(src[k] + size_t(next) * row_bytes + size_t(col[k]) * 16);
         }
         const float wq = wave_sum(ssq);
         const float wk = wave_sum(ssk);
@@ -520,11 +538,8 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
             wave_sums[parity][1][tid >> 6] = wk;
         }
         __syncthreads();
-        float tq = 0.0f, tk = 0.0f;
-        for (int i = 0; i < nwaves; ++i) {
-            tq += wave_sums[parity][0][i];
-            tk += wave_sums[parity][1][i];
-        }
+        const float tq = sum_wave_partials(wave_sums[parity][0], nwaves, tid);
+        const float tk = sum_wave_partials(wave_sums[parity][1], nwaves, tid);
         const float rq = rsqrtf(tq / float(W * q_size) + p.eps);
         const float rk = rsqrtf(tk / float(W * kv_size) + p.eps);
 #pragma unroll
@@ -546,15 +561,15 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     }
 }
 
-// Kernel entry with flat arguments; the first eight (12 dwords: the sizes and
-// the first four shards) are preloaded into SGPRs at wave launch.
+// Kernel entry with flat arguments; the first eight (14 dwords: the sizes, the
+// first four shards and both weights) are preloaded into SGPRs at wave launch,
+// so every load of a token is issued without waiting for an address.
 template <typename IO, int W, int PPL, bool LOOP>
 __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(
-    int32_t shards_used, int32_t q_packs, int32_t kv_packs, int32_t row_bytes, const uint8_t *x0,
-    const uint8_t *x1, const uint8_t *x2, const uint8_t *x3, const uint8_t *x4,
-    const uint8_t *x5, const uint8_t *x6, const uint8_t *x7, const uint8_t *q_weight,
-    const uint8_t *k_weight, uint8_t *q_out, uint8_t *k_out, int64_t T, float eps, int32_t block,
-    int32_t grid) {
+    int32_t q_packs, int32_t kv_packs, const uint8_t *x0, const uint8_t *x1, const uint8_t *x2,
+    const uint8_t *x3, const uint8_t *q_weight, const uint8_t *k_weight, const uint8_t *x4,
+    const uint8_t *x5, const uint8_t *x6, const uint8_t *x7, uint8_t *q_out, uint8_t *k_out,
+    int64_t T, float eps, int32_t grid) {
     QkParams p;
     p.x0 = x0; p.x1 = x1; p.x2 = x2; p.x3 = x3;
     p.x4 = x4; p.x5 = x5; p.x6 = x6; p.x7 = x7;
@@ -564,12 +579,9 @@ __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(
     p.q_out = q_out;
     p.k_out = k_out;
     p.T = T;
-    p.W = shards_used;
     p.q_packs = q_packs;
     p.kv_packs = kv_packs;
-    p.row_bytes = row_bytes;
     p.eps = eps;
-    p.block = block;
     p.grid = grid;
     qknorm<IO, W, PPL, LOOP>(p, shards);
 }
@@ -580,14 +592,14 @@ using QkLaunch = hipError_t (*)(const QkParams &, unsigned, unsigned, hipStream_
 
 template <typename IO, int W, int PPL, int MODE, bool QUANT, bool RES, bool ROUND>
 hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStream_t s) {
+    if (int(block) != lanes_for(p.packs, PPL)) return hipErrorInvalidConfiguration;
     RmsParams a = p;
-    a.block = int32_t(block);
     a.grid = int32_t(grid);
     void *args[] = {&a.residual, &a.weight, &a.H, &a.options,
                     &a.partials[0], &a.partials[1], &a.partials[2], &a.partials[3],
                     &a.partials[4], &a.partials[5], &a.partials[6], &a.partials[7],
                     &a.norm_out, &a.residual_out, &a.q_out, &a.scales, &a.T, &a.eps,
-                    &a.group_lanes, &a.block, &a.grid,
+                    &a.group_lanes, &a.grid,
                     &a.partials[8], &a.partials[9], &a.partials[10], &a.partials[11],
                     &a.partials[12], &a.partials[13], &a.partials[14], &a.partials[15]};
     return hipLaunchKernel(
@@ -597,13 +609,13 @@ hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStre
 
 template <typename IO, int W, int PPL, bool LOOP>
 hipError_t launch_qk(const QkParams &p, unsigned grid, unsigned block, hipStream_t s) {
+    if (int(block) != lanes_for(W * (p.q_packs + p.kv_packs), PPL))
+        return hipErrorInvalidConfiguration;
     QkParams a = p;
-    a.block = int32_t(block);
     a.grid = int32_t(grid);
-    void *args[] = {&a.W, &a.q_packs, &a.kv_packs, &a.row_bytes,
-                    &a.x0, &a.x1, &a.x2, &a.x3, &a.x4, &a.x5, &a.x6, &a.x7,
-                    &a.q_weight, &a.k_weight, &a.q_out, &a.k_out, &a.T, &a.eps, &a.block,
-                    &a.grid};
+    void *args[] = {&a.q_packs, &a.kv_packs, &a.x0, &a.x1, &a.x2, &a.x3,
+                    &a.q_weight, &a.k_weight, &a.x4, &a.x5, &a.x6, &a.x7,
+                    &a.q_out, &a.k_out, &a.T, &a.eps, &a.grid};
     return hipLaunchKernel(reinterpret_cast<const void *>(&qknorm_kernel<IO, W, PPL, LOOP>),
                            dim3(grid), dim3(block), args, 0, s);
 }
@@ -842,10 +854,8 @@ extern "C" int ar_qknorm_run(const ar_rms_plan_s *plan, const void *const *qkv, 
     p.q_out = static_cast<uint8_t *>(q_out);
     p.k_out = static_cast<uint8_t *>(k_out);
     p.T = plan->T;
-    p.W = plan->W;
     p.q_packs = q_size / kPackElems;
     p.kv_packs = kv_size / kPackElems;
-    p.row_bytes = int32_t(plan->H * 2);
     p.eps = eps;
     Shape s = qk_shape(plan->W, q_size, kv_size);
     // one workgroup per token; beyond 65536 tokens workgroups loop over tokens
