@@ -202,6 +202,33 @@ def main():
     floor_us, _ = graph_time(torch, fill, 20, 2, len(Ts) * spg, stream)
     log(f"[bench] launch floor (1-element fill kernel, graph): {floor_us:.3f} us")
 
+    # a minimal kernel that touches a row: torch's elementwise add of two
+    # [1, H] rows into a third, replayed the same way
+    a_row = torch.randn(1, wl.H, device=dev).to(torch.bfloat16)
+    b_row = torch.randn(1, wl.H, device=dev).to(torch.bfloat16)
+    c_row = torch.empty_like(a_row)
+
+    def add_row():
+        for _ in range(len(Ts) * spg):
+            torch.add(a_row, b_row, out=c_row)
+    add_us, _ = graph_time(torch, add_row, 20, 2, len(Ts) * spg, stream)
+    log(f"[bench] one-row add kernel (graph): {add_us:.3f} us")
+
+    # plain stream launches (no graph): host-bound, one ctypes call and one
+    # hipLaunchKernel per fused call
+    with torch.cuda.stream(stream):
+        for _ in range(20):
+            step()
+        stream.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(200):
+            step()
+        ev1.record(stream)
+        ev1.synchronize()
+    eager_us = ev0.elapsed_time(ev1) * 1000.0 / (200 * len(Ts))
+    log(f"[bench] plain stream launches: {eager_us:.3f} us/call")
+
     traffic = None
     rocprof_us = None
     if os.path.exists(TRAFFIC_FILE):
@@ -247,6 +274,8 @@ def main():
                    "W": W, "H": H, "T": list(Ts), "calls_per_step": len(Ts),
                    "per_T_us_per_call": per_t,
                    "launch_floor_us": round(floor_us, 3),
+                   "one_row_add_kernel_us": round(add_us, 3),
+                   "us_per_call_stream_launch": round(eager_us, 3),
                    "steps_per_graph": spg,
                    "us_per_call_one_step_per_graph": round(us_one_step_graph, 4)},
         "roofline": roofline,
