@@ -379,12 +379,23 @@ def test_graph_capture_replays_match_eager():
     qinp = cuda_inputs(WORKLOADS["c4"], 32)
     eager_q = arrms.fused_allreduce_rms_norm_quant(qinp["partials"], qinp["residual"],
                                                    qinp["weight"], 1e-6, 128)
+    # a persistent split launch whose workgroups loop over rows, and QK-norm
+    linp = cuda_inputs(GENERIC, 3000, W=8, H=4096, seed=5, device_draw=True)
+    eager_l = run_rms(linp, 1e-5, False, flags=arrms.FORCE_SPLIT)
+    wl5 = WORKLOADS["c5"]
+    kinp = to_cuda(workloads.make_qk_inputs(wl5, 64))
+    eager_k = arrms.fused_qk_norm(kinp["shards"], kinp["q_weight"], kinp["k_weight"],
+                                  wl5.q_size, wl5.kv_size, wl5.eps)
     torch.cuda.synchronize()
     plan = arrms.cached_plan(wl.W, 8, wl.H, arrms.BF16)
     qplan = arrms.cached_plan(4, 32, 7168, arrms.BF16)
+    lplan = arrms.cached_plan(8, 3000, 4096, arrms.BF16, arrms.FORCE_SPLIT)
+    kplan = arrms.cached_plan(wl5.W, 64, wl5.H, arrms.BF16)
     norm = torch.empty_like(eager[0])
     res = torch.empty_like(eager[1])
     qn, qq, qs, qr = (torch.empty_like(t) for t in eager_q)
+    ln, lr = (torch.empty_like(t) for t in eager_l)
+    kq, kk = (torch.empty_like(t) for t in eager_k)
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
@@ -393,8 +404,13 @@ def test_graph_capture_replays_match_eager():
                              norm, res, stream=s)
             arrms.ar_rms_quant_run(qplan, qinp["partials"], qinp["residual"], qinp["weight"],
                                    1e-6, False, 128, qn, qq, qs, qr, stream=s)
+            arrms.ar_rms_run(lplan, linp["partials"], linp["residual"], linp["weight"], 1e-5,
+                             False, ln, lr, stream=s)
+            arrms.ar_qknorm_run(kplan, kinp["shards"], wl5.q_size, wl5.kv_size,
+                                kinp["q_weight"], kinp["k_weight"], wl5.eps, kq, kk, stream=s)
     for _ in range(3):
-        norm.fill_(0)
+        for t in (norm, ln, kq, kk):
+            t.fill_(0)
         qq.view(torch.uint8).fill_(0)
         g.replay()
         torch.cuda.synchronize()
@@ -402,6 +418,10 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(res.view(torch.int16), eager[1].view(torch.int16))
         assert torch.equal(qq.view(torch.uint8), eager_q[1].view(torch.uint8))
         assert torch.equal(qs, eager_q[2])
+        assert torch.equal(ln.view(torch.int16), eager_l[0].view(torch.int16))
+        assert torch.equal(lr.view(torch.int16), eager_l[1].view(torch.int16))
+        assert torch.equal(kq.view(torch.int16), eager_k[0].view(torch.int16))
+        assert torch.equal(kk.view(torch.int16), eager_k[1].view(torch.int16))
         _ = (inp["partials"][0].float() * 2).sum().item()   # eager work between replays
 
 
@@ -421,8 +441,34 @@ def test_errors_leave_outputs_untouched():
     assert e.value.code == arrms.EINVAL
     with pytest.raises(ValueError):
         arrms.ar_rms_run(plan, [x, x[:4]], x, w, 1e-6, False, norm, res)
+    # quant: unsupported group size, misaligned scales
+    q = torch.full((8, 1024), 7, dtype=torch.uint8, device=DEV)
+    sc = torch.full((8, 8), 7.0, device=DEV)
+    with pytest.raises(arrms.ArrmsError) as e:
+        arrms.ar_rms_quant_run(plan, [x, x], x, w, 1e-6, False, 96, norm, q, sc, res)
+    assert e.value.code == arrms.ENOTSUP
+    qbuf = torch.full((8 * 1024 + 1,), 7, dtype=torch.uint8, device=DEV)
+    with pytest.raises(arrms.ArrmsError) as e:     # codes need 8-byte alignment
+        arrms.ar_rms_quant_run(plan, [x, x], x, w, 1e-6, False, 128, norm, qbuf[1:], sc, res)
+    assert e.value.code == arrms.EINVAL
+    # QK: k size not a multiple of 256, negative eps
+    qkv = torch.randn(8, 2048, device=DEV).to(torch.bfloat16)
+    qplan = arrms.ar_rms_plan(2, 8, 2048)
+    qw = torch.ones(2 * 1536, dtype=torch.bfloat16, device=DEV)
+    kw = torch.ones(2 * 256, dtype=torch.bfloat16, device=DEV)
+    qo = torch.full((2, 8, 1536), 7.0, dtype=torch.bfloat16, device=DEV)
+    ko = torch.full((2, 8, 256), 7.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(arrms.ArrmsError) as e:     # raw addresses: the library decides
+        arrms.ar_qknorm_run(qplan, [qkv, qkv], 1792, 128, qw.data_ptr(), kw.data_ptr(), 1e-6,
+                            qo.data_ptr(), ko.data_ptr())
+    assert e.value.code == arrms.ENOTSUP
+    with pytest.raises(arrms.ArrmsError) as e:
+        arrms.ar_qknorm_run(qplan, [qkv, qkv], 1536, 256, qw, kw, -1.0, qo, ko)
+    assert e.value.code == arrms.EINVAL
     torch.cuda.synchronize()
     assert bool((norm == 7.0).all()) and bool((res == 7.0).all())
+    assert bool((q == 7).all()) and bool((sc == 7.0).all()) and bool((qbuf == 7).all())
+    assert bool((qo == 7.0).all()) and bool((ko == 7.0).all())
 
 
 # ------------------------------------- persistent loops (more rows than workgroups)
