@@ -1,0 +1,33 @@
+"""The host-only unit of libarrms (plans, predicate, argument checks) built with
+AddressSanitizer and UndefinedBehaviorSanitizer and driven over valid, boundary
+and extreme arguments (tests/host/plan_checks.cpp).  CPU only."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "tp_all_reduce_amd", "csrc")
+
+
+def test_plan_unit_under_sanitizers(tmp_path):
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = str(tmp_path / "plan_checks")
+    cmd = [cxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "host", "plan_checks.cpp"),
+           os.path.join(CSRC, "plan.cpp"), "-o", exe]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    if build.returncode != 0 and "cannot find" in build.stderr and "asan" in build.stderr:
+        pytest.skip("sanitizer runtimes are not installed")
+    assert build.returncode == 0, build.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    env.pop("LD_PRELOAD", None)
+    run = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert run.stdout.startswith("OK"), run.stdout
