@@ -266,11 +266,12 @@ def main():
     line = {
         "metric": METRIC, "value": round(us_per_call, 4), "unit": "µs/call", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "c2 decode sweep: W=4 partials [T,4096] bf16, Gemma RMSNorm, "
                                "eps 1e-6, T in {1,2,4,8,16,21,22,32,64,80}, row-resident kernel; "
                                "one step = 10 fused calls, graph-replayed",
+                   "io_dtype": "bf16",
                    "W": W, "H": H, "T": list(Ts), "calls_per_step": len(Ts),
                    "per_T_us_per_call": per_t,
                    "launch_floor_us": round(floor_us, 3),
