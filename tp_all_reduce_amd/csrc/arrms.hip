@@ -15,20 +15,24 @@
 //            hold the group, scale = amax / 448, E4M3FN codes by the hardware
 //            conversion).
 // The row stays in registers between the phases, so HBM sees each input once
-// and each output once: (W + 2) * T * H * 2 bytes plus the weight.
+// and each output once: (W + 3) * T * H * 2 bytes (W partials and the residual
+// read, residual_out and norm_out written) plus the weight.
 //
-// Two launch shapes of the same kernel (chosen by the plan):
-//   row-resident  one workgroup per token row, one 16-byte pack per lane (up
-//                 to 1024 lanes = 8192 elements); lowest latency for the
-//                 decode window, where the launch and one DRAM round trip are
-//                 the whole cost;
-//   split         a persistent grid sized to what the CUs hold at once; each
-//                 workgroup loops over rows and issues the next row's loads
-//                 before it reduces and normalises the current one, so HBM
-//                 stays busy through the barrier and the epilogue.
+// Kernel bodies (the plan picks the launch; see Mode below):
+//   row        one workgroup per token row, one 16-byte pack per lane (up to
+//              1024 lanes = 8192 elements), straight-line code; lowest
+//              latency for the decode window, where the launch and one DRAM
+//              round trip are the whole cost;
+//   split      a persistent grid sized to what the CUs hold at once; each
+//              workgroup loops over rows and issues the next row's loads
+//              before it reduces and normalises the current one, so HBM
+//              stays busy through the barrier and the epilogue;
+//   split-wide persistent without the row-ahead loads, for rows that leave
+//              no registers for a second row (longer than 8192 elements, or
+//              more than eight partials).
 // Partials and residual are streamed with non-temporal loads (read once); the
-// weight row is loaded once per workgroup, after the first row's loads are in
-// flight, and kept in registers.
+// weight row is loaded once per workgroup and kept in registers (split-wide
+// reloads it per row from L2).
 //
 // There is no inter-workgroup communication, no atomics and no scratch
 // memory: every output is a fixed function of the inputs and bit-identical
