@@ -314,25 +314,30 @@ def test_rounding_ties_and_subnormals_bit_exact():
             check_rms(inp, norm, res, 1e-6, False, fmt=FMT[dtype])
 
 
-def test_special_values():
+@pytest.mark.parametrize("dtype,big", [(torch.bfloat16, 1e15), (torch.float16, 1e3)],
+                         ids=["bf16", "fp16"])
+@pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
+def test_special_values(dtype, big, flags):
     # eps = 0 on non-zero rows; an all-zero row with eps > 0; an inf in a row
     # (that row's residual_out keeps the inf, its norm is NaN at the inf and 0
     # elsewhere, exactly as the oracle's definition gives); large finite values
+    # (scaled to stay finite in the format)
     W, T, H = 2, 6, 512
-    inp = cuda_inputs(GENERIC, T, W=W, H=H, seed=99)
+    inp = cuda_inputs(GENERIC, T, dtype, W=W, H=H, seed=99)
     inp["partials"][0][1].zero_()
     inp["partials"][1][1].zero_()
     inp["residual"][1].zero_()
     inp["partials"][0][2, 7] = float("inf")
-    inp["partials"][1][3] *= 1e15
+    inp["partials"][1][3] *= big
+    assert bool(torch.isfinite(inp["partials"][1][3]).all())
     for eps in (0.0, 1e-6):
         if eps == 0.0:
             sel = [0, 2, 3, 4, 5]      # the zero row has 0/0 with eps = 0
         else:
             sel = list(range(T))
-        norm, res = run_rms(inp, eps, False)
+        norm, res = run_rms(inp, eps, False, flags=flags)
         torch.cuda.synchronize()
-        check_rms(inp, norm, res, eps, False, rows=np.array(sel))
+        check_rms(inp, norm, res, eps, False, rows=np.array(sel), fmt=FMT[dtype])
 
 
 @pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
