@@ -260,9 +260,12 @@ def main():
         log(f"[bench]   {large_t}")
 
     cpu = None
+    cpu_all = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cases, wl, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu}")
+        cpu_all = cpu_oracle_all_cores(cases, wl, args.cpu_seconds / 2)
+        log(f"[bench] cpu oracle, all cores: {cpu_all}")
 
     secondary = {}
     if args.full:
@@ -289,6 +292,7 @@ def main():
                    "us_per_call_one_step_per_graph": round(us_one_step_graph, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_oracle_all_cores": cpu_all,
         "large_t": large_t,
     }
     print(json.dumps(line), flush=True)
@@ -320,8 +324,61 @@ def cpu_baseline(cases, wl, seconds):
     us = el * 1e6 / (reps * len(host))
     del np
     return {"value": round(us, 2), "unit": "µs/call", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"the full c2 sweep (10 calls, T=1..80) repeated {reps} times "
                       f"({el:.1f} s, one thread)"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_oracle_all_cores(cases, wl, seconds, max_threads=16):
+    """The same oracle on every host core the process may use (at most
+    max_threads): each call's rows are split into one contiguous block per
+    thread (rows are independent, so the numbers are those of one call), and
+    the threads run the unchanged oracle side by side (the ctypes call releases
+    the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    from tp_all_reduce_amd.workloads import bits
+
+    n = max(1, min(len(os.sched_getaffinity(0)), max_threads))
+    host = [([bits(p) for p in inp["partials"]], bits(inp["residual"]), bits(inp["weight"]))
+            for T, inp, plan, norm, res in cases]
+    work = [[] for _ in range(n)]
+    for P, R, w in host:
+        T = R.shape[0]
+        for i in range(n):
+            lo, hi = T * i // n, T * (i + 1) // n
+            if hi > lo:
+                work[i].append(([p[lo:hi] for p in P], R[lo:hi], w))
+
+    def run(items):
+        for P, R, w in items:
+            oracle.ar_rms(P, R, w, wl.eps, True, want_exact=False)
+
+    reps = 0
+    with ThreadPoolExecutor(n) as pool:
+        list(pool.map(run, work))                     # warm-up round
+        t0 = time.perf_counter()
+        while True:
+            list(pool.map(run, work))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    us = el * 1e6 / (reps * len(host))
+    return {"value": round(us, 2), "unit": "µs/call", "cores": n, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"the full c2 sweep, each call's rows split over {n} threads, "
+                      f"repeated {reps} times ({el:.1f} s)"}
 
 
 def time_rms(torch, arrms, workloads, wl, T, dev, stream):
