@@ -105,16 +105,18 @@ def graph_time(torch, launch, reps, warmup, calls_per_rep, stream):
         stream.synchronize()
         with torch.cuda.graph(g, stream=stream):
             launch()
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        g.replay()
-    end.record()
+    with torch.cuda.stream(stream):   # replays and both events on the same stream
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
     end.synchronize()
+    torch.cuda.synchronize()
     ms = start.elapsed_time(end)
     return ms * 1000.0 / (reps * calls_per_rep), ms
 
