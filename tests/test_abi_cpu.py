@@ -237,3 +237,17 @@ def test_zero_tokens_accept_null_activation_pointers():
     # with tokens present the same NULLs are errors
     plan8 = arrms.ar_rms_plan(2, 8, 1024)
     assert lib.ar_rms_run(plan8.handle, ptrs, None, A, 1e-6, 0, A, None, None) == arrms.EINVAL
+
+
+def test_binding_device_and_stream_checks():
+    import torch
+    # raw addresses name no device; a stream of another device is refused
+    assert arrms._device_of([A, A], A, None) is None
+
+    class FakeStream:
+        device = torch.device("cuda", 1)
+        cuda_stream = 0
+    with pytest.raises(ValueError):
+        arrms._stream(FakeStream(), torch.device("cuda", 0))
+    assert arrms._stream(FakeStream(), torch.device("cuda", 1)) == 0
+    assert arrms._stream(1234) == 1234

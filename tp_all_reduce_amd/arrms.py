@@ -159,11 +159,31 @@ def _ptr_array(xs, what, numel, dtype):
     return arr
 
 
-def _stream(stream):
+def _device_of(*args):
+    """The one device of the tensor arguments (lists are flattened), or None if
+    every argument is a raw address.  Tensors on different devices are refused:
+    the kernel runs on one device and dereferences every pointer there."""
+    dev = None
+    for a in args:
+        for x in (a if isinstance(a, (list, tuple)) else (a,)):
+            if isinstance(x, torch.Tensor) and x.is_cuda:
+                if dev is None:
+                    dev = x.device
+                elif x.device != dev:
+                    raise ValueError(f"tensors on {dev} and {x.device}: all arguments of one "
+                                     "call must be on the same device")
+    return dev
+
+
+def _stream(stream, device=None):
+    """hipStream_t handle: the given stream, else torch's current stream of the
+    arguments' device (of the current device for raw addresses)."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
+    if device is not None and stream.device != device:
+        raise ValueError(f"stream on {stream.device}, tensors on {device}")
     return stream.cuda_stream
 
 
@@ -176,7 +196,7 @@ def ar_rms_run(plan: Plan, partials, residual, weight, eps: float, gemma: bool,
         plan.handle, _ptr_array(partials, "partials", n, dt), _addr(residual, "residual", n, dt),
         _addr(weight, "weight", plan.H, dt), float(eps), int(bool(gemma)),
         _addr(norm_out, "norm_out", n, dt), _addr(residual_out, "residual_out", n, dt),
-        _stream(stream)))
+        _stream(stream, _device_of(partials, residual, weight, norm_out, residual_out))))
 
 
 def ar_rms_quant_run(plan: Plan, partials, residual, weight, eps: float, gemma: bool,
@@ -196,7 +216,9 @@ def ar_rms_quant_run(plan: Plan, partials, residual, weight, eps: float, gemma: 
         _addr(weight, "weight", plan.H, dt), float(eps), int(bool(gemma)), int(group_size),
         _addr(norm_out, "norm_out", n, dt), _addr(q_out, "q_out", n),
         _addr(scales, "scales", n_scales, torch.float32),
-        _addr(residual_out, "residual_out", n, dt), _stream(stream)))
+        _addr(residual_out, "residual_out", n, dt),
+        _stream(stream, _device_of(partials, residual, weight, norm_out, q_out, scales,
+                                   residual_out))))
 
 
 def ar_qknorm_run(plan: Plan, qkv, q_size: int, kv_size: int, q_weight, k_weight, eps: float,
@@ -209,7 +231,8 @@ def ar_qknorm_run(plan: Plan, qkv, q_size: int, kv_size: int, q_weight, k_weight
         plan.handle, _ptr_array(qkv, "qkv", T * plan.H, dt), int(q_size), int(kv_size),
         _addr(q_weight, "q_weight", W * q_size, dt), _addr(k_weight, "k_weight", W * kv_size, dt),
         float(eps), _addr(q_out, "q_out", W * T * q_size, dt),
-        _addr(k_out, "k_out", W * T * kv_size, dt), _stream(stream)))
+        _addr(k_out, "k_out", W * T * kv_size, dt),
+        _stream(stream, _device_of(qkv, q_weight, k_weight, q_out, k_out))))
 
 
 # ------------------------------------------------------ tensor-level helpers
