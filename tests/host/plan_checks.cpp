@@ -131,6 +131,27 @@ int main() {
     expect(check_qk_args(many, nine, 256, 256, addr(A), addr(A), 1e-6f, addr(A), addr(A)) == ARRMS_ENOTSUP, "QK W > 8");
     ar_rms_plan_destroy(many);
 
+    // QK lane layouts: shards on whole wavefronts when that fits one workgroup
+    long aligned = 0, packed = 0;
+    for (int W = 1; W <= 8; ++W)
+        for (int q = 256; q <= 32768; q += 256)
+            for (int kv = 256; kv <= 32768; kv += 256) {
+                if (int64_t(W) * (q + kv) > 32768) continue;
+                const arrms::Shape a = arrms::qk_aligned_shape(W, q, kv);
+                const arrms::Shape b = arrms::qk_shape(W, q, kv);
+                const int per_shard = (q + kv) / 8;
+                expect(b.block % 64 == 0 && b.block <= 1024 && int64_t(b.block) * b.ppl >= W * per_shard,
+                       "packed shape", W, q, kv);
+                if (a.block == 0) { ++packed; continue; }
+                ++aligned;
+                const int lanes = a.block / W;
+                expect(a.block % W == 0 && lanes % 64 == 0 && a.block <= 1024, "aligned block", W, q, kv);
+                expect(a.ppl == 1 || a.ppl == 2 || a.ppl == 4, "aligned ppl", W, q, kv);
+                expect(int64_t(lanes) * a.ppl >= per_shard && lanes - 64 < (per_shard + a.ppl - 1) / a.ppl,
+                       "aligned lanes cover a shard", W, q, kv);
+            }
+    expect(aligned > 0 && packed > 0, "both QK layouts occur", aligned, packed);
+
     std::printf("%s: %ld plans built, %d failures\n", failures ? "FAILED" : "OK", plans, failures);
     return failures ? 1 : 0;
 }

@@ -224,8 +224,11 @@ def test_quant_fp16_gemma_codes_only():
     check_quant(inp, 1e-6, True, 128, outs, fmt=oracle.FP16)
 
 
+# the last two shapes do not fit every shard on whole wavefronts in 1024 lanes
+# and take the packed lane layout
 @pytest.mark.parametrize("W,T,q,kv", [(1, 3, 256, 256), (2, 17, 512, 256), (8, 5, 1024, 256),
-                                      (4, 130, 1536, 256), (3, 7, 2048, 512)])
+                                      (4, 130, 1536, 256), (3, 7, 2048, 512), (5, 9, 1024, 768),
+                                      (8, 4, 2048, 512), (3, 9, 8192, 2304), (7, 6, 4096, 512)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 def test_qk_shapes(W, T, q, kv, dtype):
     inp = workloads.make_qk_inputs(WORKLOADS["c5"], T, dtype, W=W, q_size=q, kv_size=kv,
@@ -541,9 +544,11 @@ def test_more_than_eight_partials_variants(variant):
         check_rms(inp, norm, None, 1e-6, False, expect_residual=False)
 
 
-def test_qk_more_tokens_than_workgroups():
-    """Beyond 65536 tokens the QK workgroups loop over tokens."""
-    W, T, q, kv = 2, 70000, 256, 256
+@pytest.mark.parametrize("W,T,q,kv", [(2, 70000, 256, 256), (3, 66000, 8192, 2304)],
+                         ids=["shard_aligned", "packed"])
+def test_qk_more_tokens_than_workgroups(W, T, q, kv):
+    """Beyond 65536 tokens the QK workgroups loop over tokens, in both lane
+    layouts (the second shape does not fit shards on whole wavefronts)."""
     inp = workloads.make_qk_inputs(WORKLOADS["c5"], T, W=W, q_size=q, kv_size=kv, seed=3,
                                    device=DEV)
     q_out, k_out = arrms.fused_qk_norm(inp["shards"], inp["q_weight"], inp["k_weight"], q, kv,

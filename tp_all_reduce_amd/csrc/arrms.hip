@@ -478,13 +478,21 @@ struct Shards {
 
 // LOOP: workgroups loop over tokens (more tokens than workgroups); without it
 // every workgroup handles exactly one token in straight-line code.
-template <typename IO, int W, int PPL, bool LOOP>
+// ALIGNED: each shard owns lanes_for(q + kv packs, PPL) lanes, a whole number
+// of wavefronts, so a wavefront's shard and base pointer are wave-uniform and
+// worked out in scalar registers; otherwise (shapes that do not fit 1024 lanes
+// that way) the packs are laid out back to back: all shards' q packs, then all
+// their k packs, and each lane finds its shard by vector comparisons.
+template <typename IO, int W, int PPL, bool LOOP, bool ALIGNED>
 __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     __shared__ float wave_sums[2][2][kMaxBlock / 64];
     const int tid = threadIdx.x;
+    const int per_shard = p.q_packs + p.kv_packs;
     const int nq = W * p.q_packs;
     const int n = nq + W * p.kv_packs;
-    const int nthr = lanes_for(n, PPL);   // launch width (see reduce_norm)
+    const int shard_lanes = lanes_for(per_shard, PPL);
+    // launch width (see reduce_norm)
+    const int nthr = ALIGNED ? W * shard_lanes : lanes_for(n, PPL);
     const int nwaves = nthr >> 6;
     const size_t row_bytes = size_t(p.q_packs + 2 * p.kv_packs) * 16;
     const int q_size = p.q_packs * 8;
@@ -494,26 +502,53 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     // no integer division), the pack's column in the shard row, the weight
     // pack, and the output row offset.  A lane past the end takes pack 0's
     // layout (every address in bounds) and is masked by `valid`.
+    // Aligned: the wave-uniform shard r and the pack's column `part` within the
+    // shard's q or k part; the weight and output addresses are each a choice
+    // between two whole q and k address expressions (a product with a per-lane
+    // q-or-k factor would be a vector multiply).  Packed: the weight pack and
+    // the output offset, worked out once per lane.
     bool valid[PPL], is_q[PPL];
     const uint8_t *src[PPL];
-    int col[PPL], widx[PPL];
+    int col[PPL], part[PPL], widx[PPL];
     size_t out_off[PPL];
-#pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-        valid[k] = tid + k * nthr < n;
-        const int pk = valid[k] ? tid + k * nthr : 0;
-        is_q[k] = pk < nq;
-        const int idx = is_q[k] ? pk : pk - nq;
-        const int per = is_q[k] ? p.q_packs : p.kv_packs;
+    int r_al = 0;
+    if constexpr (ALIGNED) {
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int shard_waves = shard_lanes >> 6;
         int r = 0;
 #pragma unroll
-        for (int i = 1; i < W; ++i) r += idx >= i * per ? 1 : 0;
-        const int j = idx - r * per;
-        widx[k] = idx;
-        col[k] = j + (is_q[k] ? 0 : p.q_packs);
-        src[k] = shards.pick<W>(r);
-        out_off[k] = size_t(r) * size_t(p.T) * size_t(is_q[k] ? q_size : kv_size) * 2 +
-                     size_t(j) * 16;
+        for (int i = 1; i < W; ++i) r += wave >= i * shard_waves ? 1 : 0;
+        const uint8_t *base = shards.pick<W>(r);
+        const int lane = tid - r * shard_lanes;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int c0 = lane + k * shard_lanes;   // column pack in the [q | k] row
+            valid[k] = c0 < per_shard;
+            const int c = valid[k] ? c0 : 0;
+            is_q[k] = c < p.q_packs;
+            col[k] = c;
+            part[k] = is_q[k] ? c : c - p.q_packs;
+            src[k] = base;
+        }
+        r_al = r;
+    } else {
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            valid[k] = tid + k * nthr < n;
+            const int pk = valid[k] ? tid + k * nthr : 0;
+            is_q[k] = pk < nq;
+            const int idx = is_q[k] ? pk : pk - nq;
+            const int per = is_q[k] ? p.q_packs : p.kv_packs;
+            int r = 0;
+#pragma unroll
+            for (int i = 1; i < W; ++i) r += idx >= i * per ? 1 : 0;
+            const int j = idx - r * per;
+            widx[k] = idx;
+            col[k] = j + (is_q[k] ? 0 : p.q_packs);
+            src[k] = shards.pick<W>(r);
+            out_off[k] = size_t(r) * size_t(p.T) * size_t(is_q[k] ? q_size : kv_size) * 2 +
+                         size_t(j) * 16;
+        }
     }
 
     int64_t row = blockIdx.x;     // < T: the launcher never starts more workgroups than rows
@@ -526,7 +561,11 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     // weights: loaded once (the same for every token), after the first loads
 #pragma unroll
     for (int k = 0; k < PPL; ++k)
-        wr[k] = load16((is_q[k] ? p.q_weight : p.k_weight) + size_t(widx[k]) * 16);
+        if constexpr (ALIGNED)
+            wr[k] = load16(is_q[k] ? p.q_weight + size_t(r_al * p.q_packs + part[k]) * 16
+                                   : p.k_weight + size_t(r_al * p.kv_packs + part[k]) * 16);
+        else
+            wr[k] = load16((is_q[k] ? p.q_weight : p.k_weight) + size_t(widx[k]) * 16);
 
     int parity = 0;
     for (;;) {
@@ -567,8 +606,17 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
                 float y[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) y[i] = (x[k][i] * rs) * wv[i];
-                const size_t row_off = size_t(row) * size_t(is_q[k] ? q_size : kv_size) * 2;
-                store16((is_q[k] ? p.q_out : p.k_out) + out_off[k] + row_off, pack8<IO>(y));
+                // q_out [W, T, q_size], k_out [W, T, kv_size]
+                uint8_t *dst;
+                if constexpr (ALIGNED) {
+                    const size_t out_row = size_t(r_al) * size_t(p.T) + size_t(row);
+                    dst = is_q[k] ? p.q_out + (out_row * p.q_packs + part[k]) * 16
+                                  : p.k_out + (out_row * p.kv_packs + part[k]) * 16;
+                } else {
+                    const size_t row_off = size_t(row) * size_t(is_q[k] ? q_size : kv_size) * 2;
+                    dst = (is_q[k] ? p.q_out : p.k_out) + out_off[k] + row_off;
+                }
+                store16(dst, pack8<IO>(y));
             }
         }
         if (!LOOP || next >= p.T) break;
@@ -580,7 +628,7 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
 // Kernel entry with flat arguments; the first eight (14 dwords: the sizes, the
 // first four shards and both weights) are preloaded into SGPRs at wave launch,
 // so every load of a token is issued without waiting for an address.
-template <typename IO, int W, int PPL, bool LOOP>
+template <typename IO, int W, int PPL, bool LOOP, bool ALIGNED>
 __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(
     int32_t q_packs, int32_t kv_packs, const uint8_t *x0, const uint8_t *x1, const uint8_t *x2,
     const uint8_t *x3, const uint8_t *q_weight, const uint8_t *k_weight, const uint8_t *x4,
@@ -599,7 +647,7 @@ __global__ __launch_bounds__(kMaxBlock) void qknorm_kernel(
     p.kv_packs = kv_packs;
     p.eps = eps;
     p.grid = grid;
-    qknorm<IO, W, PPL, LOOP>(p, shards);
+    qknorm<IO, W, PPL, LOOP, ALIGNED>(p, shards);
 }
 
 // ------------------------------------------------------------- launchers
@@ -623,16 +671,17 @@ hipError_t launch_rms(const RmsParams &p, unsigned grid, unsigned block, hipStre
         dim3(grid), dim3(block), args, 0, s);
 }
 
-template <typename IO, int W, int PPL, bool LOOP>
+template <typename IO, int W, int PPL, bool LOOP, bool ALIGNED>
 hipError_t launch_qk(const QkParams &p, unsigned grid, unsigned block, hipStream_t s) {
-    if (int(block) != lanes_for(W * (p.q_packs + p.kv_packs), PPL))
-        return hipErrorInvalidConfiguration;
+    const int per_shard = p.q_packs + p.kv_packs;
+    const int lanes = ALIGNED ? W * lanes_for(per_shard, PPL) : lanes_for(W * per_shard, PPL);
+    if (int(block) != lanes) return hipErrorInvalidConfiguration;
     QkParams a = p;
     a.grid = int32_t(grid);
     void *args[] = {&a.q_packs, &a.kv_packs, &a.x0, &a.x1, &a.x2, &a.x3,
                     &a.q_weight, &a.k_weight, &a.x4, &a.x5, &a.x6, &a.x7,
                     &a.q_out, &a.k_out, &a.T, &a.eps, &a.grid};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&qknorm_kernel<IO, W, PPL, LOOP>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&qknorm_kernel<IO, W, PPL, LOOP, ALIGNED>),
                            dim3(grid), dim3(block), args, 0, s);
 }
 
@@ -712,34 +761,35 @@ Variant pick_rms(int dtype, int W, int mode, bool quant, bool res, bool round) {
                                : pick_io<Fp16>(W, mode, quant, res, round);
 }
 
-template <typename IO, int W, bool LOOP>
+template <typename IO, int W, bool LOOP, bool ALIGNED>
 QkLaunch pick_qk_ppl(int ppl) {
     switch (ppl) {
-    case 1: return &launch_qk<IO, W, 1, LOOP>;
-    case 2: return &launch_qk<IO, W, 2, LOOP>;
-    case 4: return &launch_qk<IO, W, 4, LOOP>;
+    case 1: return &launch_qk<IO, W, 1, LOOP, ALIGNED>;
+    case 2: return &launch_qk<IO, W, 2, LOOP, ALIGNED>;
+    case 4: return &launch_qk<IO, W, 4, LOOP, ALIGNED>;
     default: return nullptr;
     }
 }
 
-template <typename IO, bool LOOP>
+template <typename IO, bool LOOP, bool ALIGNED>
 QkLaunch pick_qk_w(int W, int ppl) {
     switch (W) {
-    case 1: return pick_qk_ppl<IO, 1, LOOP>(ppl);
-    case 2: return pick_qk_ppl<IO, 2, LOOP>(ppl);
-    case 3: return pick_qk_ppl<IO, 3, LOOP>(ppl);
-    case 4: return pick_qk_ppl<IO, 4, LOOP>(ppl);
-    case 5: return pick_qk_ppl<IO, 5, LOOP>(ppl);
-    case 6: return pick_qk_ppl<IO, 6, LOOP>(ppl);
-    case 7: return pick_qk_ppl<IO, 7, LOOP>(ppl);
-    case 8: return pick_qk_ppl<IO, 8, LOOP>(ppl);
+    case 1: return pick_qk_ppl<IO, 1, LOOP, ALIGNED>(ppl);
+    case 2: return pick_qk_ppl<IO, 2, LOOP, ALIGNED>(ppl);
+    case 3: return pick_qk_ppl<IO, 3, LOOP, ALIGNED>(ppl);
+    case 4: return pick_qk_ppl<IO, 4, LOOP, ALIGNED>(ppl);
+    case 5: return pick_qk_ppl<IO, 5, LOOP, ALIGNED>(ppl);
+    case 6: return pick_qk_ppl<IO, 6, LOOP, ALIGNED>(ppl);
+    case 7: return pick_qk_ppl<IO, 7, LOOP, ALIGNED>(ppl);
+    case 8: return pick_qk_ppl<IO, 8, LOOP, ALIGNED>(ppl);
     default: return nullptr;
     }
 }
 
 template <typename IO>
-QkLaunch pick_qk(int W, int ppl, bool loop) {
-    return loop ? pick_qk_w<IO, true>(W, ppl) : pick_qk_w<IO, false>(W, ppl);
+QkLaunch pick_qk(int W, int ppl, bool loop, bool aligned) {
+    if (aligned) return loop ? pick_qk_w<IO, true, true>(W, ppl) : pick_qk_w<IO, false, true>(W, ppl);
+    return loop ? pick_qk_w<IO, true, false>(W, ppl) : pick_qk_w<IO, false, false>(W, ppl);
 }
 
 // Workgroups of the split kernel that the device holds at once (CUs times
@@ -873,13 +923,16 @@ extern "C" int ar_qknorm_run(const ar_rms_plan_s *plan, const void *const *qkv, 
     p.q_packs = q_size / kPackElems;
     p.kv_packs = kv_size / kPackElems;
     p.eps = eps;
-    Shape s = qk_shape(plan->W, q_size, kv_size);
+    // shards on whole wavefronts when that fits, else packs back to back
+    Shape s = qk_aligned_shape(plan->W, q_size, kv_size);
+    const bool aligned = s.block != 0;
+    if (!aligned) s = qk_shape(plan->W, q_size, kv_size);
     // one workgroup per token; beyond 65536 tokens workgroups loop over tokens
     const int64_t max_grid = 65536;
     const bool loop = plan->T > max_grid;
     const int64_t grid = loop ? max_grid : plan->T;
-    QkLaunch fn = plan->dtype == ARRMS_BF16 ? pick_qk<Bf16>(plan->W, s.ppl, loop)
-                                            : pick_qk<Fp16>(plan->W, s.ppl, loop);
+    QkLaunch fn = plan->dtype == ARRMS_BF16 ? pick_qk<Bf16>(plan->W, s.ppl, loop, aligned)
+                                            : pick_qk<Fp16>(plan->W, s.ppl, loop, aligned);
     if (fn == nullptr) return fail(ARRMS_ENOTSUP, "no QK kernel for %d packs per lane", s.ppl);
     hipError_t e = fn(p, unsigned(grid), unsigned(s.block), static_cast<hipStream_t>(stream));
     if (e != hipSuccess)

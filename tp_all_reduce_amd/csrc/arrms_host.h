@@ -43,6 +43,7 @@ struct Shape {
 Shape row_shape(int64_t H);
 Shape split_shape(int64_t H);
 Shape qk_shape(int W, int q_size, int kv_size);
+Shape qk_aligned_shape(int W, int q_size, int kv_size);   // {0, 0}: does not fit
 
 // Argument checks of the run entry points; return ARRMS_OK or the status to
 // return (with the message recorded).

@@ -52,6 +52,18 @@ Shape split_shape(int64_t H) {
     return Shape{block, ppl};
 }
 
+// QK-norm with every shard on whole wavefronts: the fewest packs per lane
+// (1, 2 or 4) for which W * lanes_for(q + kv packs) fits one workgroup;
+// {0, 0} when none does.
+Shape qk_aligned_shape(int W, int q_size, int kv_size) {
+    const int per_shard = (q_size + kv_size) / kPackElems;
+    for (int ppl = 1; ppl <= kMaxQkPpl; ppl *= 2) {
+        const int lanes = round_up((per_shard + ppl - 1) / ppl, 64);
+        if (int64_t(W) * lanes <= kMaxBlock) return Shape{W * lanes, ppl};
+    }
+    return Shape{0, 0};
+}
+
 Shape qk_shape(int W, int q_size, int kv_size) {
     int packs = W * (q_size + kv_size) / kPackElems;
     int ppl = next_pow2((packs + kMaxBlock - 1) / kMaxBlock);
