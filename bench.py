@@ -302,7 +302,6 @@ def main():
 
 def cpu_baseline(cases, wl, seconds):
     """The oracle as it stands, single-threaded, on the same sweep."""
-    import numpy as np
     import oracle
     from oracle import compare
     from tp_all_reduce_amd.workloads import bits
@@ -324,7 +323,6 @@ def cpu_baseline(cases, wl, seconds):
         if el >= seconds:
             break
     us = el * 1e6 / (reps * len(host))
-    del np
     return {"value": round(us, 2), "unit": "µs/call", "cores": 1, "kind": "oracle",
             "cpu": cpu_model(),
             "sample": f"the full c2 sweep (10 calls, T=1..80) repeated {reps} times "
