@@ -544,8 +544,9 @@ def test_more_than_eight_partials_variants(variant):
         check_rms(inp, norm, None, 1e-6, False, expect_residual=False)
 
 
-@pytest.mark.parametrize("W,T,q,kv", [(2, 70000, 256, 256), (3, 66000, 8192, 2304)],
-                         ids=["shard_aligned", "packed"])
+@pytest.mark.parametrize("W,T,q,kv", [(2, 70000, 256, 256), (8, 66000, 2048, 512),
+                                      (3, 66000, 8192, 2304)],
+                         ids=["shard_aligned", "shard_aligned_4_per_lane", "packed"])
 def test_qk_more_tokens_than_workgroups(W, T, q, kv):
     """Beyond 65536 tokens the QK workgroups loop over tokens, in both lane
     layouts (the second shape does not fit shards on whole wavefronts)."""
