@@ -450,6 +450,13 @@ def full_report(torch, arrms, workloads, WORKLOADS, dev, stream, args):
             else:
                 out[key] = time_rms(torch, arrms, workloads, wl, T, dev, stream)
             log(f"[bench]   {out[key]}")
+    if not args.only:
+        # beyond the pages' eight ranks: 16 partial buffers at the prefill row
+        # length (the persistent body without row-ahead loads)
+        w16 = workloads.Workload("w16", 9, W=16, H=8192, Ts=(4096,), eps=1e-5)
+        log("[bench] w16_T4096")
+        out["w16_T4096"] = time_rms(torch, arrms, workloads, w16, 4096, dev, stream)
+        log(f"[bench]   {out['w16_T4096']}")
     return out
 
 
