@@ -30,9 +30,9 @@
 //   split-wide persistent without the row-ahead loads, for rows that leave
 //              no registers for a second row (longer than 8192 elements, or
 //              more than eight partials).
-// Partials and residual are streamed with non-temporal loads (read once); the
-// weight row is loaded once per workgroup and kept in registers (split-wide
-// reloads it per row from L2).
+// The looping bodies stream partials and residual with non-temporal loads
+// (read once); the weight row is loaded once per workgroup and kept in
+// registers (split-wide reloads it per row from L2).
 //
 // There is no inter-workgroup communication, no atomics and no scratch
 // memory: every output is a fixed function of the inputs and bit-identical
@@ -215,11 +215,13 @@ __host__ __device__ constexpr int lanes_for(int packs, int ppl) {
 }
 
 // Issues the loads of one row: W partial packs and (RES) the residual pack for
-// each of the lane's PPL packs (pack pk = lane + k * workgroup size).  A lane
+// each of the lane's PPL packs (pack pk = lane + k * workgroup size), with the
+// non-temporal hint in the looping (large-T) bodies; the row body's inputs are
+// small and may still be cached from the op that wrote them.  A lane
 // past the row's end loads pack 0 of the row instead (its sum is zeroed and
 // nothing of it is stored): with no branch around a load, the compiler places
 // no wait at a join.
-template <int W, int PPL, bool RES>
+template <int W, int PPL, bool RES, bool STREAM>
 __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int tid, int nthr,
                                          u32x4 (&v)[PPL][W + RES]) {
     const size_t base = size_t(row) * size_t(p.H) * 2;
@@ -228,8 +230,10 @@ __device__ __forceinline__ void load_row(const RmsParams &p, int64_t row, int ti
         const int pk = tid + k * nthr;
         const size_t off = base + size_t(pk < p.packs ? pk : 0) * 16;
 #pragma unroll
-        for (int r = 0; r < W; ++r) v[k][r] = load16_stream(p.partials[r] + off);
-        if constexpr (RES) v[k][W] = load16_stream(p.residual + off);
+        for (int r = 0; r < W; ++r)
+            v[k][r] = STREAM ? load16_stream(p.partials[r] + off) : load16(p.partials[r] + off);
+        if constexpr (RES)
+            v[k][W] = STREAM ? load16_stream(p.residual + off) : load16(p.residual + off);
     }
     // Keep every load ahead of what follows: the scheduler would otherwise put
     // one behind the wait for the scalar load of the output pointers.
@@ -270,7 +274,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     constexpr int NB = W + RES;      // packs loaded per lane pack: partials, residual
     // kSplit: `ahead` receives the next row's loads one row in advance
     u32x4 ahead[PPL][NB];
-    if constexpr (MODE == kSplit) load_row<W, PPL, RES>(p, row, tid, nthr, ahead);
+    if constexpr (MODE == kSplit) load_row<W, PPL, RES, MODE != kRow>(p, row, tid, nthr, ahead);
     // weight row: loaded once per workgroup and kept (kSplitWide reloads it
     // per row from L2 after the row's reduction, to stay within registers);
     // converted where used, so no wait on it stands before the row's loads
@@ -293,9 +297,9 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
             for (int k = 0; k < PPL; ++k)
 #pragma unroll
                 for (int r = 0; r < NB; ++r) cur[k][r] = ahead[k][r];
-            if (next < p.T) load_row<W, PPL, RES>(p, next, tid, nthr, ahead);
+            if (next < p.T) load_row<W, PPL, RES, MODE != kRow>(p, next, tid, nthr, ahead);
         } else {
-            load_row<W, PPL, RES>(p, row, tid, nthr, cur);
+            load_row<W, PPL, RES, MODE != kRow>(p, row, tid, nthr, cur);
         }
         const size_t base = size_t(row) * size_t(p.H) * 2;
 
