@@ -408,7 +408,7 @@ def time_rms(torch, arrms, workloads, wl, T, dev, stream):
             else:
                 arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
                                  wl.gemma, norm, res, stream=stream)
-    us, _ = graph_time(torch, call, 10 if big else 50, 2, n_calls, stream)
+    us, _ = graph_time(torch, call, 10 if big else 50, 2 if big else 20, n_calls, stream)
     nbytes = rms_bytes(wl.W, T, wl.H, wl.group)
     gbs = nbytes / (us * 1e-6) / 1e9
     out = {"us_per_call": round(us, 3), "bytes": nbytes, "GB_s": round(gbs, 1),
@@ -429,7 +429,7 @@ def time_qk(torch, arrms, workloads, wl, T, dev, stream):
         for _ in range(20):
             arrms.ar_qknorm_run(plan, inp["shards"], wl.q_size, wl.kv_size, inp["q_weight"],
                                 inp["k_weight"], wl.eps, qo, ko, stream=stream)
-    us, _ = graph_time(torch, call, 50, 2, 20, stream)
+    us, _ = graph_time(torch, call, 50, 20, 20, stream)
     nbytes = 2 * wl.W * T * (wl.q_size + wl.kv_size) * 2 + wl.W * (wl.q_size + wl.kv_size) * 2
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"us_per_call": round(us, 3), "bytes": nbytes, "GB_s": round(gbs, 1),
