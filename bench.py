@@ -79,7 +79,8 @@ def parse():
     ap.add_argument("--steps-per-graph", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large-t", action="store_true",
-                    help="skip the W=8 [8192, 8192] prefill figure reported beside the headline")
+                    help="skip the figures of the other workloads reported beside the headline "
+                         "(prefill W=8 [8192, 8192], c1, c3 T=1024, c4, c5)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--full", default=None,
                     help="also time every workload (c1..c5) and write a JSON report here")
@@ -261,6 +262,18 @@ def main():
                        workload="W=8 partials [8192, 8192] bf16, eps 1e-5, split kernel")
         log(f"[bench]   {large_t}")
 
+    # the other workloads, one line each (same graph method; bytes algorithmic)
+    others = None
+    if not args.no_large_t:
+        others = {}
+        for name, T in (("c1", 8), ("c3", 1024), ("c4", 256), ("c5", 64)):
+            wl_o = WORKLOADS[name]
+            r = (time_qk if name == "c5" else time_rms)(torch, arrms, workloads, wl_o, T, dev,
+                                                         stream)
+            others[f"{name}_T{T}"] = {"us_per_call": r["us_per_call"], "GB_s": r["GB_s"],
+                                      "frac_of_peak": r["frac_of_peak"], "kernel": r["kernel"]}
+        log(f"[bench] other workloads: {others}")
+
     cpu = None
     cpu_all = None
     if not args.no_cpu_baseline:
@@ -296,6 +309,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_oracle_all_cores": cpu_all,
         "large_t": large_t,
+        "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
 
