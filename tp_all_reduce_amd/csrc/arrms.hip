@@ -502,15 +502,14 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
     const int q_size = p.q_packs * 8;
     const int kv_size = p.kv_packs * 8;
 
-    // Row-independent lane layout, worked out once: shard r (by comparisons,
-    // no integer division), the pack's column in the shard row, the weight
-    // pack, and the output row offset.  A lane past the end takes pack 0's
+    // Row-independent lane layout, worked out once: each pack's shard (by
+    // comparisons, no integer division) and its column in the shard row.
+    // Aligned: the shard r_al is wave-uniform and `part` is the column within
+    // the shard's q or k part; the weight and output addresses are each a
+    // choice between two whole q and k address expressions (a product with a
+    // per-lane q-or-k factor would be a vector multiply).  Packed: the weight
+    // pack and the output offset per lane.  A lane past the end takes pack 0's
     // layout (every address in bounds) and is masked by `valid`.
-    // Aligned: the wave-uniform shard r and the pack's column `part` within the
-    // shard's q or k part; the weight and output addresses are each a choice
-    // between two whole q and k address expressions (a product with a per-lane
-    // q-or-k factor would be a vector multiply).  Packed: the weight pack and
-    // the output offset, worked out once per lane.
     bool valid[PPL], is_q[PPL];
     const uint8_t *src[PPL];
     int col[PPL], part[PPL], widx[PPL];
