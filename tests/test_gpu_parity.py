@@ -635,3 +635,68 @@ def test_round_reduced_worked_case(flags):
     torch.cuda.synchronize()
     assert torch.all(r_fused == 1.0 + 2.0 ** -7)
     assert torch.all(r_round == 1.0)
+
+
+# ------------------------------------------- seeded random configurations
+def random_config(seed):
+    """One call's configuration drawn from everything the library accepts."""
+    rng = np.random.default_rng(seed)
+    dtype = [torch.bfloat16, torch.float16][rng.integers(2)]
+    W = int(rng.integers(1, 17))
+    max_packs = 1024 if W > 8 else 2048
+    H = 8 * int(rng.integers(1, max_packs + 1))
+    T = int(rng.choice([0, 1, 2, 3, 7, 31, 80, 81, 129, 300]))
+    quant = bool(rng.random() < 0.4)
+    group = 0
+    if quant:
+        choices = [g for g in (8, 16, 32, 64, 128, 256, 512) if H % g == 0]
+        group = int(rng.choice(choices))
+    kinds = ["default", "split"]
+    if W <= 8 and T <= 80 and H <= 8192:
+        kinds.append("row")
+    kind = kinds[rng.integers(len(kinds))]
+    return dict(dtype=dtype, W=W, H=H, T=T, group=group, kind=kind,
+                gemma=bool(rng.random() < 0.5), residual=["yes", "none", "dead"][rng.integers(3)],
+                round_reduced=bool(rng.random() < 0.3), with_norm=bool(rng.random() < 0.7))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_configurations(seed):
+    c = random_config(seed)
+    print(f"[random] seed {seed}: {c}", flush=True)
+    flags = {"default": 0, "split": arrms.FORCE_SPLIT, "row": arrms.FORCE_ROW}[c["kind"]]
+    inp = cuda_inputs(GENERIC, c["T"], c["dtype"], W=c["W"], H=c["H"], seed=10_000 + seed)
+    if c["residual"] == "none":
+        inp["residual"] = None
+    residual_out = None if c["residual"] == "dead" else "new"
+    fmt = FMT[c["dtype"]]
+    T, H = c["T"], c["H"]
+    rows = np.arange(T)
+    P = [host_rows(p, rows) for p in inp["partials"]]
+    R = None if inp["residual"] is None else host_rows(inp["residual"], rows)
+    if c["group"]:
+        outs = arrms.fused_allreduce_rms_norm_quant(
+            inp["partials"], inp["residual"], inp["weight"], 1e-6, c["group"], c["gemma"],
+            with_norm=c["with_norm"], residual_out=residual_out, flags=flags,
+            round_reduced=c["round_reduced"])
+        torch.cuda.synchronize()
+        norm, q, sc, res = outs
+        _, c_o, s_o, r_o, exact = oracle.ar_rms_quant(P, R, bits(inp["weight"]), 1e-6, c["gemma"],
+                                                      c["group"], fmt,
+                                                      round_reduced=c["round_reduced"])
+        assert compare.max_code_distance(q.view(torch.uint8).reshape(T, H).cpu().numpy(), c_o) <= 1
+        assert compare.max_scale_relerr(sc.reshape(T, H // c["group"]).cpu().numpy(),
+                                        s_o) <= compare.SCALE_TOL
+    else:
+        norm, res = arrms.fused_allreduce_rms_norm(
+            inp["partials"], inp["residual"], inp["weight"], 1e-6, c["gemma"],
+            residual_out=residual_out, flags=flags, round_reduced=c["round_reduced"])
+        torch.cuda.synchronize()
+        _, r_o, exact = oracle.ar_rms(P, R, bits(inp["weight"]), 1e-6, c["gemma"], fmt,
+                                      round_reduced=c["round_reduced"])
+    if norm is not None:
+        assert compare.max_relerr(host_rows(norm, rows), exact, fmt) <= compare.TOL[fmt]
+    if res is None:
+        assert c["residual"] == "dead"
+    else:
+        assert compare.bits_equal(host_rows(res, rows), r_o)
