@@ -700,3 +700,25 @@ def test_random_configurations(seed):
         assert c["residual"] == "dead"
     else:
         assert compare.bits_equal(host_rows(res, rows), r_o)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_qk_configurations(seed):
+    """QK-norm over shapes drawn from the whole accepted domain (both lane
+    layouts, one to four packs per lane)."""
+    rng = np.random.default_rng(50_000 + seed)
+    while True:
+        W = int(rng.integers(1, 9))
+        q = 256 * int(rng.integers(1, 33))
+        kv = 256 * int(rng.integers(1, 17))
+        if W * (q + kv) <= 32768:
+            break
+    T = int(rng.choice([1, 2, 5, 17, 64]))
+    dtype = [torch.bfloat16, torch.float16][rng.integers(2)]
+    print(f"[random qk] seed {seed}: W={W} T={T} q={q} kv={kv} {dtype}", flush=True)
+    inp = to_cuda(workloads.make_qk_inputs(WORKLOADS["c5"], T, dtype, W=W, q_size=q, kv_size=kv,
+                                           seed=60_000 + seed))
+    q_out, k_out = arrms.fused_qk_norm(inp["shards"], inp["q_weight"], inp["k_weight"], q, kv,
+                                       1e-6)
+    torch.cuda.synchronize()
+    check_qk(inp, q, kv, 1e-6, q_out, k_out, FMT[dtype])
