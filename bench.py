@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = ("µs/call at T<=80 and effective HBM GB/s (% of MI355X peak) for W-way "
           "reduce+add-RMSNorm")
-KERNEL_SRC = os.path.join(ROOT, "tp_all_reduce_amd", "csrc", "arrms.hip")
+KERNEL_SRC = os.path.join(ROOT, "tp_all_reduce_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_kernel_c2_sweep.json")
 
 
@@ -61,14 +61,19 @@ def rms_bytes(W, T, H, group=0, residual=True):
 
 
 def kernel_source_sha(path: str = KERNEL_SRC) -> str:
-    """Hash of the kernel source's code: comments and whitespace are dropped, so
-    a comment edit does not void the recorded counters (the source holds no
-    string literal with a comment marker)."""
-    src = open(path, encoding="utf-8").read()
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", " ", src)
-    code = " ".join(src.split())
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    """Hash of the code of every source file of the library (the kernel units,
+    their headers, the run unit and the plan code, in name order): comments and
+    whitespace are dropped, so a comment edit does not void the recorded
+    counters (the sources hold no string literal with a comment marker)."""
+    parts = []
+    for name in sorted(os.listdir(path)):
+        if not name.endswith((".hip", ".h", ".cpp")):
+            continue
+        src = open(os.path.join(path, name), encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        parts.append(name + ": " + " ".join(src.split()))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()[:16]
 
 
 def parse():

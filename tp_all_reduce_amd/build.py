@@ -1,5 +1,7 @@
 """Builds libarrms.so in-tree: the host-only plan/validation unit with the host
-C++ compiler, the HIP unit with hipcc for gfx950, linked by hipcc.
+C++ compiler, the run unit and the six kernel units (each instantiates one
+slice of the kernel variants) with hipcc for gfx950, all compiled in
+parallel, then linked by hipcc.
 
     python -m tp_all_reduce_amd.build
 """
@@ -9,6 +11,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -32,19 +35,34 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
 
 
+# The run unit (entry points, no device code) and the kernel units.
+HIP_UNITS = ["arrms", "rms_bf16", "rms_bf16_fp8", "rms_fp16", "rms_fp16_fp8", "qk_bf16", "qk_fp16"]
+
+
 def _run(cmd):
     print("+", " ".join(cmd), flush=True)
     subprocess.check_call(cmd)
 
 
+def _jobs() -> int:
+    for var in ("MAX_JOBS", "CMAKE_BUILD_PARALLEL_LEVEL"):
+        if os.environ.get(var, "").isdigit() and int(os.environ[var]) > 0:
+            return int(os.environ[var])
+    return os.cpu_count() or 1
+
+
 def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
-    plan_o = os.path.join(BUILD, "plan.o")
-    hip_o = os.path.join(BUILD, "arrms.o")
-    _run([CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
-    _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "arrms.hip"), "-o", hip_o])
+    cmds = [[CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"),
+             "-o", os.path.join(BUILD, "plan.o")]]
+    cmds += [[HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, u + ".hip"),
+              "-o", os.path.join(BUILD, u + ".o")] for u in HIP_UNITS]
+    with ThreadPoolExecutor(max_workers=max(1, min(_jobs(), len(cmds)))) as pool:
+        for f in [pool.submit(_run, c) for c in cmds]:
+            f.result()
+    objs = [c[-1] for c in cmds]
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", plan_o, hip_o, "-o", tmp])
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 
