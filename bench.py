@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--no-large-t", action="store_true",
                     help="skip the figures of the other workloads reported beside the headline "
                          "(prefill W=8 [8192, 8192], c1, c3 T=1024, c4, c5)")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip timing the unfused PyTorch composition (profiled runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--full", default=None,
                     help="also time every workload (c1..c5) and write a JSON report here")
@@ -264,8 +266,10 @@ def main():
     # sum in bf16 by chained adds (what a separate all-reduce hands over), then
     # the residual add (residual_out) and torch's rms_norm with the Gemma
     # weight 1 + w (formed before the timed region); replayed the same way
-    unfused = unfused_sweep(torch, cases, wl, spg, stream)
-    log(f"[bench] unfused PyTorch composition (graph): {unfused}")
+    unfused = None
+    if not args.no_unfused:
+        unfused = unfused_sweep(torch, cases, wl, spg, stream)
+        log(f"[bench] unfused PyTorch composition (graph): {unfused}")
 
     # plain stream launches (no graph): host-bound, one ctypes call and one
     # hipLaunchKernel per fused call

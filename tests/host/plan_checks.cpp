@@ -149,6 +149,15 @@ int main() {
                 expect(a.ppl == 1 || a.ppl == 2 || a.ppl == 4, "aligned ppl", W, q, kv);
                 expect(int64_t(lanes) * a.ppl >= per_shard && lanes - 64 < (per_shard + a.ppl - 1) / a.ppl,
                        "aligned lanes cover a shard", W, q, kv);
+                // the fewest packs per lane that fit, except that four or more
+                // shards filling 1024 lanes at one pack per lane take two
+                int want = 0;
+                for (int ppl = 1; ppl <= 4 && want == 0; ppl *= 2) {
+                    const int l = ((per_shard + ppl - 1) / ppl + 63) / 64 * 64;
+                    if (W * l > 1024 || (ppl == 1 && W >= 4 && W * l == 1024)) continue;
+                    want = ppl;
+                }
+                expect(a.ppl == want, "aligned ppl choice", W, q, kv);
             }
     expect(aligned > 0 && packed > 0, "both QK layouts occur", aligned, packed);
 

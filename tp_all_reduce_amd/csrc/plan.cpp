@@ -54,12 +54,17 @@ Shape split_shape(int64_t H) {
 
 // QK-norm with every shard on whole wavefronts: the fewest packs per lane
 // (1, 2 or 4) for which W * lanes_for(q + kv packs) fits one workgroup;
-// {0, 0} when none does.
+// {0, 0} when none does.  Exception, from measurement: four or more shards
+// that would fill all 1024 lanes with one pack per lane take two (sixteen
+// wavefronts ran 2-10 % slower than eight there; with fewer shards, or fewer
+// wavefronts, halving the wavefronts ran as fast or slower).
 Shape qk_aligned_shape(int W, int q_size, int kv_size) {
     const int per_shard = (q_size + kv_size) / kPackElems;
     for (int ppl = 1; ppl <= kMaxQkPpl; ppl *= 2) {
         const int lanes = round_up((per_shard + ppl - 1) / ppl, 64);
-        if (int64_t(W) * lanes <= kMaxBlock) return Shape{W * lanes, ppl};
+        if (int64_t(W) * lanes > kMaxBlock) continue;
+        if (ppl == 1 && W >= 4 && W * lanes == kMaxBlock) continue;
+        return Shape{W * lanes, ppl};
     }
     return Shape{0, 0};
 }
