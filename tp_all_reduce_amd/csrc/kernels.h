@@ -21,7 +21,7 @@
 // and each output once: (W + 3) * T * H * 2 bytes (W partials and the residual
 // read, residual_out and norm_out written) plus the weight.
 //
-// Kernel bodies (the plan picks the launch; see Mode below):
+// Kernel bodies (the plan picks the launch; see Mode in launch.h):
 //   row        one workgroup per token row, one 16-byte pack per lane (up to
 //              1024 lanes = 8192 elements), straight-line code; lowest
 //              latency for the decode window, where the launch and one DRAM
