@@ -169,6 +169,20 @@ __device__ __forceinline__ float sum_wave_partials(const float *ws, int n, int l
     return row16_sum(i < n ? ws[i] : 0.0f);
 }
 
+// The q and k statistics of QK-norm: the sums of the first n (<= 16) entries of
+// `a` and of `b`, the same bits in every lane.  Lane i reads entry i mod 16 of
+// both (0 from n on), so both LDS reads are in flight together and the two
+// 16-lane DPP sums interleave: for two statistics this measured faster than two
+// index-order loops, each with its own LDS round trip.  Both arrays hold 16
+// entries.
+__device__ __forceinline__ f32x2 sum_wave_partials2(const float *a, const float *b, int n,
+                                                   int lane) {
+    const int i = lane & 15;
+    const float x = a[i];
+    const float y = b[i];
+    return f32x2{row16_sum(i < n ? x : 0.0f), row16_sum(i < n ? y : 0.0f)};
+}
+
 // Max over aligned groups of `lanes` consecutive lanes (1..64, a power of two);
 // every lane of a group ends with the group's max.
 __device__ __forceinline__ float group_max(float v, int lanes) {
@@ -546,10 +560,9 @@ __device__ __forceinline__ void qknorm(const QkParams &p, const Shards shards) {
             wave_sums[parity][1][tid >> 6] = wk;
         }
         __syncthreads();
-        const float tq = sum_wave_partials(wave_sums[parity][0], nwaves, tid);
-        const float tk = sum_wave_partials(wave_sums[parity][1], nwaves, tid);
-        const float rq = rsqrtf(tq / float(W * q_size) + p.eps);
-        const float rk = rsqrtf(tk / float(W * kv_size) + p.eps);
+        const f32x2 t = sum_wave_partials2(wave_sums[parity][0], wave_sums[parity][1], nwaves, tid);
+        const float rq = rsqrtf(t.x / float(W * q_size) + p.eps);
+        const float rk = rsqrtf(t.y / float(W * kv_size) + p.eps);
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
             if (valid[k]) {
