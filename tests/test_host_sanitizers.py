@@ -27,7 +27,6 @@ def test_plan_unit_under_sanitizers(tmp_path):
     assert build.returncode == 0, build.stderr
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0",
                UBSAN_OPTIONS="print_stacktrace=1")
-    env.pop("LD_PRELOAD", None)
     run = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
     assert run.returncode == 0, run.stdout + run.stderr
     assert run.stdout.startswith("OK"), run.stdout
