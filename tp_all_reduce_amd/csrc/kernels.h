@@ -183,9 +183,20 @@ __device__ __forceinline__ f32x2 sum_wave_partials2(const float *a, const float 
     return f32x2{row16_sum(i < n ? x : 0.0f), row16_sum(i < n ? y : 0.0f)};
 }
 
+// Max over aligned groups of 16 consecutive lanes (128-element groups of 16-bit
+// data), in straight-line code.
+__device__ __forceinline__ float group_max16(float v) {
+    v = fmaxf(v, dpp<kQuadSwap1>(v));
+    v = fmaxf(v, dpp<kQuadSwap2>(v));
+    v = fmaxf(v, dpp<kHalfMirror>(v));
+    return fmaxf(v, dpp<kRowMirror>(v));
+}
+
 // Max over aligned groups of `lanes` consecutive lanes (1..64, a power of two);
-// every lane of a group ends with the group's max.
+// every lane of a group ends with the group's max.  The common 16-lane group
+// takes one uniform branch instead of a test per step.
 __device__ __forceinline__ float group_max(float v, int lanes) {
+    if (lanes == 16) return group_max16(v);
     if (lanes >= 2) v = fmaxf(v, dpp<kQuadSwap1>(v));
     if (lanes >= 4) v = fmaxf(v, dpp<kQuadSwap2>(v));
     if (lanes >= 8) v = fmaxf(v, dpp<kHalfMirror>(v));
@@ -193,6 +204,19 @@ __device__ __forceinline__ float group_max(float v, int lanes) {
     if (lanes >= 32) v = fmaxf(v, __shfl_xor(v, 16));
     if (lanes >= 64) v = fmaxf(v, __shfl_xor(v, 32));
     return v;
+}
+
+// amax / 448 correctly rounded, in three instructions where the quotient is a
+// normal number: the product with c = RN(1/448) and one FMA correction equal the
+// IEEE quotient for every such input (checked exhaustively on the CPU); below
+// 2^-116, and for inf, the division.
+__device__ __forceinline__ float div448(float amax) {
+    if (amax >= 0x1p-116f && amax <= 3.40282347e38f) {
+        const float c = 1.0f / 448.0f;
+        const float q = amax * c;
+        return __builtin_fmaf(__builtin_fmaf(-q, 448.0f, amax), c, q);
+    }
+    return amax / 448.0f;
 }
 
 // Four fp32 values -> four OCP FP8 E4M3FN codes (byte i = value i), rounded to
@@ -268,6 +292,10 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     };
     if constexpr (MODE != kSplitWide) load_weight();
 
+    // 1/H for the FP8 variant, formed while the row's loads are in flight: its
+    // epilogue's dependent chain is long enough that the division after the
+    // barrier measured slower (the plain variant divides there: measured faster)
+    float inv_h = 1.0f / float(p.H);
     int parity = 0;
     for (;;) {
         u32x4 cur[PPL][NB];
@@ -281,6 +309,8 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
         } else {
             load_row<W, PPL, RES, MODE != kRow>(p, row, tid, nthr, cur);
         }
+        // keeps the compiler from moving the division next to its use
+        if constexpr (QUANT) asm volatile("" : "+v"(inv_h));
         const size_t base = size_t(row) * size_t(p.H) * 2;
 
         // phase 1: rank-ordered fp32 sum, residual last, residual_out
@@ -325,7 +355,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
             // rows of several packs per lane have registers for nothing more
             for (int i = 0; i < nwaves; ++i) total += wave_sums[parity][i];
         }
-        const float rstd = rsqrtf(total / float(p.H) + p.eps);
+        const float rstd = rsqrtf((QUANT ? total * inv_h : total / float(p.H)) + p.eps);
 
         // phase 2: normalise, weight, store; optional FP8 group epilogue
         if constexpr (MODE == kSplitWide) load_weight();
@@ -356,15 +386,17 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
                 amax = group_max(amax, p.group_lanes);
-                const float scale = amax / 448.0f;
+                const float scale = div448(amax);
                 uint32_t lo = 0, hi = 0;
                 if (scale != 0.0f) {
-                    // One division per lane, then products: y * (1 / scale) is within
-                    // one fp32 rounding of y / scale.  Since |y| <= amax, every
-                    // quotient is at most 448 * (1 + 3 * 2^-24) and rounds to at
-                    // most 448: no saturation step is needed.  A scale below about
-                    // 2^-128 has no finite reciprocal; those groups divide.
-                    const float inv = 1.0f / scale;
+                    // The hardware reciprocal (v_rcp_f32, within 1 ulp), then
+                    // products: y * inv is within two fp32 roundings of y / scale,
+                    // so a code can move one step at a rounding boundary.  Since
+                    // |y| <= amax, every quotient is at most 448 * (1 + 2^-22) and
+                    // rounds to at most 448: no saturation step is needed.  A scale
+                    // below about 2^-128 has no finite reciprocal; those groups
+                    // divide.
+                    const float inv = __builtin_amdgcn_rcpf(scale);
                     if (__builtin_expect(inv <= 3.40282347e38f, 1)) {
                         lo = pack4_e4m3(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
                         hi = pack4_e4m3(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
