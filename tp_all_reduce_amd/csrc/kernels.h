@@ -208,8 +208,9 @@ __device__ __forceinline__ float group_max(float v, int lanes) {
 
 // amax / 448 correctly rounded, in three instructions where the quotient is a
 // normal number: the product with c = RN(1/448) and one FMA correction equal the
-// IEEE quotient for every such input (checked exhaustively on the CPU); below
-// 2^-116, and for inf, the division.
+// IEEE quotient for every such input (checked over every float on the CPU, and
+// by the CPU tests over the binades at the guard); below 2^-116, where some
+// subnormal quotients differ, and for inf, the division.
 __device__ __forceinline__ float div448(float amax) {
     if (amax >= 0x1p-116f && amax <= 3.40282347e38f) {
         const float c = 1.0f / 448.0f;
