@@ -566,13 +566,17 @@ def test_qk_more_tokens_than_workgroups(W, T, q, kv):
 @pytest.mark.parametrize("flags", [arrms.FORCE_ROW, arrms.FORCE_SPLIT], ids=["row", "split"])
 def test_quant_tiny_and_zero_scales(flags):
     """Groups whose scale is subnormal (amax/448 below 2^-126, reciprocal beyond
-    fp32), a group of zero weights (scale 0, codes 0) and ordinary groups."""
+    fp32), a group of zero weights (scale 0, codes 0), groups just above the
+    kernel's 2^-116 guard for the division-free scale and far up the range, and
+    ordinary groups."""
     W, T, H, G = 2, 9, 1024, 128
     inp = cuda_inputs(WORKLOADS["c4"], T, W=W, H=H, seed=11)
     w = inp["weight"].float()
     w[:G] = w[:G] * 1e-37          # tiny: normalised values ~1e-37
     w[G:2 * G] = 0.0               # zero group
     w[2 * G:3 * G] = w[2 * G:3 * G] * 3e-36
+    w[3 * G:4 * G] = w[3 * G:4 * G] * 2.0 ** -114   # amax a few times 2^-114
+    w[5 * G:6 * G] = w[5 * G:6 * G] * 1e36          # amax ~1e36
     inp["weight"] = w.to(torch.bfloat16)
     outs = arrms.fused_allreduce_rms_norm_quant(inp["partials"], inp["residual"], inp["weight"],
                                                 1e-6, G, flags=flags)
@@ -581,6 +585,9 @@ def test_quant_tiny_and_zero_scales(flags):
     scales = outs[2].cpu().numpy()
     assert np.all(scales[:, 1] == 0) and np.all(scales[:, 0] < 2.0 ** -126)
     assert np.all(outs[1].view(torch.uint8).cpu().numpy()[:, G:2 * G] == 0)
+    # the division-free scale at both ends of its range
+    assert np.all(scales[:, 3] >= 2.0 ** -116 / 448) and np.all(scales[:, 3] < 2.0 ** -116)
+    assert np.all(scales[:, 5] > 1e32)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
