@@ -591,6 +591,39 @@ def test_quant_tiny_and_zero_scales(flags):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("W", [4, 6, 8])
+@pytest.mark.parametrize("form", ["residual", "gemma", "no_residual", "dead_residual",
+                                  "round_reduced"])
+def test_split_band_of_few_rows_per_workgroup(W, form, dtype):
+    """Split plans of 512 to 8 x (resident workgroups) rows, where four to eight
+    partials without the FP8 epilogue may run on twice the workgroups per CU
+    without the row-ahead loads: every form of the call at rows of 8192 (one
+    workgroup per CU otherwise) and 4096 elements."""
+    fmt = FMT[dtype]
+    for H, T in ((8192, 1500), (4096, 2500)):
+        inp = cuda_inputs(WORKLOADS["c3"], T, dtype, W=W, H=H, seed=W * 100 + T,
+                          device_draw=True)
+        gemma = form == "gemma"
+        if form == "no_residual":
+            inp["residual"] = None
+        norm, res = arrms.fused_allreduce_rms_norm(
+            inp["partials"], inp["residual"], inp["weight"], 1e-5, gemma,
+            residual_out=None if form == "dead_residual" else "new",
+            round_reduced=form == "round_reduced")
+        torch.cuda.synchronize()
+        rows = sample_rows(T, 160, seed=T)
+        P = [host_rows(p, rows) for p in inp["partials"]]
+        R = None if inp["residual"] is None else host_rows(inp["residual"], rows)
+        n, r, exact = oracle.ar_rms(P, R, bits(inp["weight"]), 1e-5, gemma, fmt,
+                                    round_reduced=form == "round_reduced")
+        assert compare.max_relerr(host_rows(norm, rows), exact, fmt) <= compare.TOL[fmt]
+        if form == "dead_residual":
+            assert res is None
+        else:
+            assert compare.bits_equal(host_rows(res, rows), r)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("flags,T", [(arrms.FORCE_ROW, 21), (arrms.FORCE_SPLIT, 21),
                                      (arrms.FORCE_SPLIT, 5000)], ids=["row", "split", "split_loop"])
 def test_round_reduced_sum(flags, T, dtype):

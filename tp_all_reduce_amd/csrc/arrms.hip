@@ -86,7 +86,19 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
     if (split) {
         const int resident = resident_grid(v.symbol, plan->block);
         if (resident <= 0) return fail(ARRMS_EHIP, "device occupancy query failed");
-        if (grid > resident) {
+        // At most eight rows per workgroup: without the FP8 epilogue, four to
+        // eight partials run faster on twice the workgroups per CU without the
+        // row-ahead loads, where the device holds that many (measured 2-4 %
+        // faster at 512 to 2048 rows; with more rows, with the FP8 epilogue or
+        // with fewer partials the row-ahead body is as fast or faster).
+        Variant lean{nullptr, nullptr};
+        if (mode == kSplit && grid > resident && grid <= 8 * int64_t(resident))
+            lean = pick_rms(plan->dtype, plan->W, kSplitLean, quant, res, round);
+        const int lean_resident = lean.launch ? resident_grid(lean.symbol, plan->block) : 0;
+        if (lean.launch && lean_resident >= 2 * resident) {
+            v = lean;
+            grid = grid < lean_resident ? grid : lean_resident;
+        } else if (grid > resident) {
             grid = resident;
         } else if (mode == kSplit) {
             mode = kRow;

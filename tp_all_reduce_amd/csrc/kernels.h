@@ -32,7 +32,9 @@
 //              stays busy through the barrier and the epilogue;
 //   split-wide persistent without the row-ahead loads, for rows that leave
 //              no registers for a second row (longer than 8192 elements, or
-//              more than eight partials).
+//              more than eight partials), and, with one pack per lane (the
+//              lean mode), for split plans of only a few rows per workgroup:
+//              its registers leave room for two workgroups per CU.
 // The looping bodies stream partials and residual with non-temporal loads
 // (read once); the weight row is loaded once per workgroup and kept in
 // registers (split-wide reloads it per row from L2).
@@ -689,13 +691,18 @@ Variant variant() {
 }
 
 // Modes built: kRow and kSplit with one pack per lane, kSplitWide with four
-// packs per lane (rows longer than 8192 elements).
+// packs per lane (rows longer than 8192 elements), kSplitLean (the kSplitWide
+// body with one pack per lane) for four to eight partials without the FP8
+// epilogue.
 template <typename IO, int W, bool QUANT, bool RES, bool ROUND>
 Variant pick_mode(int mode) {
     switch (mode) {
     case kRow: return variant<IO, W, 1, kRow, QUANT, RES, ROUND>();
     case kSplit: return variant<IO, W, 1, kSplit, QUANT, RES, ROUND>();
     case kSplitWide: return variant<IO, W, kMaxPpl, kSplitWide, QUANT, RES, ROUND>();
+    case kSplitLean:
+        if constexpr (!QUANT && W >= 4) return variant<IO, W, 1, kSplitWide, QUANT, RES, ROUND>();
+        return Variant{nullptr, nullptr};
     default: return Variant{nullptr, nullptr};
     }
 }

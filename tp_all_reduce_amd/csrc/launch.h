@@ -49,8 +49,11 @@ constexpr int32_t kGemma = 1;         // weight applied as 1 + w (Gemma RMSNorm)
 // ahead.  kSplitWide: persistent, loads at the top of each row, for shapes that
 // leave no room in registers for a second row: four packs per lane (rows
 // longer than 8192 elements), or one pack per lane with more than eight
-// partials.
-enum Mode { kRow = 0, kSplit = 1, kSplitWide = 2 };
+// partials.  kSplitLean: the kSplitWide body with one pack per lane for four to
+// eight partials without the FP8 epilogue; it needs few enough registers for
+// two workgroups per CU, which beats the row-ahead loads when each workgroup
+// would get only a few rows.
+enum Mode { kRow = 0, kSplit = 1, kSplitWide = 2, kSplitLean = 3 };
 
 // ------------------------------------------------------------- QK-norm
 struct QkParams {
