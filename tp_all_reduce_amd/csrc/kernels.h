@@ -185,13 +185,30 @@ __device__ __forceinline__ f32x2 sum_wave_partials2(const float *a, const float 
     return f32x2{row16_sum(i < n ? x : 0.0f), row16_sum(i < n ? y : 0.0f)};
 }
 
+// The group maxima below take per-lane maxima of magnitudes: non-negative
+// floats that are never NaN (a lane's maximum starts at 0 and fmaxf skips NaN).
+// On those, the order of the bit patterns as unsigned integers is the order of
+// the values, so each step is one unsigned max with a DPP operand; a float max
+// would first quiet its operands (three instructions and a move per step).
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_dpp(uint32_t v) {
+    const uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+    return v > o ? v : o;
+}
+
+__device__ __forceinline__ uint32_t umax_xor(uint32_t v, int lane_mask) {
+    const uint32_t o = uint32_t(__shfl_xor(int(v), lane_mask));
+    return v > o ? v : o;
+}
+
 // Max over aligned groups of 16 consecutive lanes (128-element groups of 16-bit
 // data), in straight-line code.
 __device__ __forceinline__ float group_max16(float v) {
-    v = fmaxf(v, dpp<kQuadSwap1>(v));
-    v = fmaxf(v, dpp<kQuadSwap2>(v));
-    v = fmaxf(v, dpp<kHalfMirror>(v));
-    return fmaxf(v, dpp<kRowMirror>(v));
+    uint32_t u = __float_as_uint(v);
+    u = umax_dpp<kQuadSwap1>(u);
+    u = umax_dpp<kQuadSwap2>(u);
+    u = umax_dpp<kHalfMirror>(u);
+    return __uint_as_float(umax_dpp<kRowMirror>(u));
 }
 
 // Max over aligned groups of `lanes` consecutive lanes (1..64, a power of two);
@@ -199,13 +216,14 @@ __device__ __forceinline__ float group_max16(float v) {
 // takes one uniform branch instead of a test per step.
 __device__ __forceinline__ float group_max(float v, int lanes) {
     if (lanes == 16) return group_max16(v);
-    if (lanes >= 2) v = fmaxf(v, dpp<kQuadSwap1>(v));
-    if (lanes >= 4) v = fmaxf(v, dpp<kQuadSwap2>(v));
-    if (lanes >= 8) v = fmaxf(v, dpp<kHalfMirror>(v));
-    if (lanes >= 16) v = fmaxf(v, dpp<kRowMirror>(v));
-    if (lanes >= 32) v = fmaxf(v, __shfl_xor(v, 16));
-    if (lanes >= 64) v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    uint32_t u = __float_as_uint(v);
+    if (lanes >= 2) u = umax_dpp<kQuadSwap1>(u);
+    if (lanes >= 4) u = umax_dpp<kQuadSwap2>(u);
+    if (lanes >= 8) u = umax_dpp<kHalfMirror>(u);
+    if (lanes >= 16) u = umax_dpp<kRowMirror>(u);
+    if (lanes >= 32) u = umax_xor(u, 16);
+    if (lanes >= 64) u = umax_xor(u, 32);
+    return __uint_as_float(u);
 }
 
 // amax / 448 correctly rounded, in three instructions where the quotient is a
