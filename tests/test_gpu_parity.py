@@ -762,3 +762,67 @@ def test_random_qk_configurations(seed):
                                        1e-6)
     torch.cuda.synchronize()
     check_qk(inp, q, kv, 1e-6, q_out, k_out, FMT[dtype])
+
+
+def test_concurrent_callers_on_their_own_streams():
+    """Four host threads, each with its own stream, shape and inputs, call the
+    library concurrently (the ctypes calls release the interpreter lock): the
+    row body, the row-ahead split, the split of few rows per workgroup and the
+    FP8 epilogue.  Each also makes one invalid call and reads its own error
+    message (the last error is per thread).  Every output matches the oracle."""
+    import threading
+    cases = [(2, 16, 1024, 0), (8, 4000, 8192, 0), (6, 1500, 8192, 0), (4, 256, 7168, 128)]
+    inputs = [cuda_inputs(WORKLOADS["c4"], T, W=W, H=H, seed=900 + i, device_draw=True)
+              for i, (W, T, H, G) in enumerate(cases)]
+    torch.cuda.synchronize()
+    results, errors = [None] * len(cases), []
+    barrier = threading.Barrier(len(cases))
+
+    def worker(i):
+        try:
+            W, T, H, G = cases[i]
+            inp = inputs[i]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                barrier.wait()
+                for _ in range(20):
+                    if G:
+                        out = arrms.fused_allreduce_rms_norm_quant(
+                            inp["partials"], inp["residual"], inp["weight"], 1e-6, G)
+                    else:
+                        out = arrms.fused_allreduce_rms_norm(inp["partials"], inp["residual"],
+                                                             inp["weight"], 1e-6)
+                    try:
+                        arrms.fused_allreduce_rms_norm(inp["partials"], inp["residual"],
+                                                       inp["weight"], float("nan"))
+                        errors.append(f"thread {i}: NaN eps accepted")
+                    except arrms.ArrmsError as e:
+                        if e.code != arrms.EINVAL or "eps" not in e.message:
+                            errors.append(f"thread {i}: wrong error {e}")
+                stream.synchronize()
+            results[i] = out
+        except Exception as e:  # reported below, with the thread
+            errors.append(f"thread {i}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a caller thread did not finish"
+    assert not errors, errors
+    for (W, T, H, G), inp, out in zip(cases, inputs, results):
+        rows = sample_rows(T, 96, seed=T)
+        if G:
+            sub = {"partials": [p.index_select(0, torch.as_tensor(rows, device=DEV))
+                                for p in inp["partials"]],
+                   "residual": inp["residual"].index_select(0, torch.as_tensor(rows, device=DEV)),
+                   "weight": inp["weight"]}
+            idx = torch.as_tensor(rows, device=DEV)
+            norm, q, scales, res = out
+            check_quant(sub, 1e-6, False, G, (norm.index_select(0, idx),
+                                              q.view(torch.uint8).index_select(0, idx),
+                                              scales.index_select(0, idx),
+                                              res.index_select(0, idx)))
+        else:
+            check_rms(inp, out[0], out[1], 1e-6, False, rows=rows)
