@@ -1,0 +1,79 @@
+"""The latency targets of the decode-window workloads, measured the benchmark's
+way (100 back-to-back calls per HIP graph, replays timed with HIP events on the
+replaying stream, inputs resident): at most 5 us per call for c1, for every T of
+the c2 sweep (row-resident kernel) and for the c5 QK-norm.  The kernels run in
+about 2-2.5 us, so the bound leaves room for slower boxes; it catches a path
+that has fallen off the fast kernels, not small drifts."""
+import os
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from tp_all_reduce_amd import arrms, workloads  # noqa: E402
+from tp_all_reduce_amd.workloads import WORKLOADS  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TARGET_US = 5.0
+
+
+def per_call_us(launch, stream):
+    us, _ = bench.graph_time(torch, launch, 10, 3, 100, stream)
+    return us
+
+
+def test_c2_every_T_within_5us():
+    wl = WORKLOADS["c2"]
+    stream = torch.cuda.Stream()
+    worst = {}
+    for T in wl.Ts:
+        inp = workloads.make_inputs(wl, T, device=DEV)
+        plan = arrms.cached_plan(wl.W, T, wl.H, arrms.BF16, arrms.FORCE_ROW)
+        norm = torch.empty_like(inp["partials"][0])
+        res = torch.empty_like(norm)
+
+        def call():
+            for _ in range(100):
+                arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
+                                 True, norm, res, stream=stream)
+        worst[T] = per_call_us(call, stream)
+    assert max(worst.values()) <= TARGET_US, worst
+
+
+def test_c1_within_5us():
+    wl = WORKLOADS["c1"]
+    stream = torch.cuda.Stream()
+    inp = workloads.make_inputs(wl, 8, device=DEV)
+    plan = arrms.cached_plan(wl.W, 8, wl.H, arrms.BF16)
+    norm = torch.empty_like(inp["partials"][0])
+    res = torch.empty_like(norm)
+
+    def call():
+        for _ in range(100):
+            arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
+                             False, norm, res, stream=stream)
+    us = per_call_us(call, stream)
+    assert us <= TARGET_US, us
+
+
+def test_c5_within_5us():
+    wl = WORKLOADS["c5"]
+    stream = torch.cuda.Stream()
+    inp = workloads.make_qk_inputs(wl, 64, device=DEV)
+    plan = arrms.cached_plan(wl.W, 64, wl.H, arrms.BF16)
+    qo = torch.empty((wl.W, 64, wl.q_size), dtype=torch.bfloat16, device=DEV)
+    ko = torch.empty((wl.W, 64, wl.kv_size), dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        for _ in range(100):
+            arrms.ar_qknorm_run(plan, inp["shards"], wl.q_size, wl.kv_size, inp["q_weight"],
+                                inp["k_weight"], wl.eps, qo, ko, stream=stream)
+    us = per_call_us(call, stream)
+    assert us <= TARGET_US, us
