@@ -1,6 +1,8 @@
 """Host-side logic of bench.py, without a GPU: the algorithmic byte count, the
-source hash that ties recorded counters to the kernel sources, and the refusal
-of runs on more than one GPU."""
+source hash that ties recorded counters to the kernel sources, the argument
+checks and step plan (run before torch is imported, so that a bad argument
+costs no GPU), and the refusal of runs on more than one GPU."""
+import json
 import os
 import shutil
 import subprocess
@@ -108,3 +110,70 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def run_bench(*argv):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
+                          capture_output=True, text=True, timeout=120)
+
+
+def test_driver_invocation_is_accepted_before_any_gpu_work():
+    """The round-end command, `bench.py --gpus 1 --steps 20 --warmup 5`, with
+    --check-args: the arguments pass, exactly 20 steps are timed after exactly
+    5 warm-up steps, and torch has not been imported by then."""
+    r = run_bench("--gpus", "1", "--steps", "20", "--warmup", "5", "--check-args")
+    assert r.returncode == 0, r.stderr
+    plan = json.loads(r.stdout)
+    assert plan["timed_steps"] == 20 and sum(plan["timed_graphs"]) == 20
+    assert plan["warmup_steps"] == 5 and sum(plan["warmup_graphs"]) == 5
+    assert plan["torch_imported"] is False
+
+
+def test_default_invocation_is_accepted():
+    r = run_bench("--check-args")
+    assert r.returncode == 0, r.stderr
+    plan = json.loads(r.stdout)
+    assert sum(plan["timed_graphs"]) == plan["timed_steps"] >= 1
+
+
+def test_bad_arguments_fail_fast_without_torch():
+    for argv, what in ((["--steps", "0"], "--steps"), (["--warmup", "-1"], "--warmup"),
+                       (["--steps-per-graph", "0"], "--steps-per-graph")):
+        r = run_bench(*argv)
+        assert r.returncode == 2, (argv, r.stderr)
+        assert what in r.stderr and r.stdout == ""
+
+
+def test_step_pieces_cover_exactly_the_requested_steps():
+    for count in range(0, 57):
+        for per in (1, 3, 10, 64):
+            p = bench.pieces(count, per)
+            assert sum(p) == count
+            assert all(1 <= n <= per for n in p)
+            # whole graphs first, at most one remainder graph, at the end
+            assert all(n == per for n in p[:-1])
+
+
+def test_cold_rotation_exceeds_the_caches():
+    """The cold figures rotate through more than 512 MiB of sets (at least
+    three), in whole graphs when there are more sets than calls per graph."""
+    for set_bytes in (81920, 1 << 20, 18_874_368, 27_596_800, 184_565_760, 600 << 20):
+        for calls in (10, 100):
+            n = bench.cold_sets(set_bytes, calls)
+            assert n >= 3
+            assert n * set_bytes > bench.COLD_BYTES or set_bytes > bench.COLD_BYTES
+            if n > calls:
+                assert n % calls == 0
+
+
+def test_pool_offsets_are_aligned_and_disjoint():
+    shapes = [(8, 1024), (3, 7), (80, 4096), (1, 8)]
+    sizes = [bench.Pool.size_of([s]) for s in shapes]
+    assert all(s % 4096 == 0 and s >= 2 * s_[0] * s_[1] for s, s_ in zip(sizes, shapes))
+    assert bench.Pool.size_of(shapes) == sum(sizes)
+    p = bench.Pool(torch, "cpu", bench.Pool.size_of(shapes), torch.bfloat16)
+    ts = [p.take(s) for s in shapes]
+    spans = [(t.data_ptr(), t.data_ptr() + t.numel() * 2) for t in ts]
+    assert all(a % 4096 == spans[0][0] % 4096 for a, _ in spans)
+    assert all(spans[i][1] <= spans[i + 1][0] for i in range(len(spans) - 1))
+    assert spans[-1][1] <= p.buf.data_ptr() + p.buf.numel() * 2

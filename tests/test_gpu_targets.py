@@ -4,7 +4,10 @@ inputs resident): at most 5 us per call for c1, for every T of the c2 sweep
 (row-resident kernel) and for the c5 QK-norm, and at least 70 % of the HBM peak
 for the c3 prefill at T=8192.  The kernels run in about 2-2.5 us and at 76-78 %,
 so the bounds leave room for slower boxes; they catch a call that has left the
-fast kernels, not small drifts."""
+fast kernels, not small drifts.  Each test prints what it measured (a
+``[target]`` line on the process's stderr, outside pytest's capture), so a
+regression shows as a number and not only as a failure."""
+import json
 import os
 import sys
 
@@ -26,8 +29,12 @@ TARGET_US = 5.0
 
 
 def per_call_us(launch, stream):
-    us, _ = bench.graph_time(torch, launch, 10, 3, 100, stream)
-    return us
+    return bench.graph_time(torch, launch, 10, 3, 100, stream)
+
+
+def report(name, **values):
+    sys.__stderr__.write("[target] " + json.dumps(dict(test=name, **values)) + "\n")
+    sys.__stderr__.flush()
 
 
 def test_c2_every_T_within_5us():
@@ -44,7 +51,8 @@ def test_c2_every_T_within_5us():
             for _ in range(100):
                 arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
                                  True, norm, res, stream=stream)
-        worst[T] = per_call_us(call, stream)
+        worst[T] = round(per_call_us(call, stream), 3)
+    report("c2_every_T", us_per_call=worst, bound_us=TARGET_US)
     assert max(worst.values()) <= TARGET_US, worst
 
 
@@ -61,6 +69,7 @@ def test_c1_within_5us():
             arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
                              False, norm, res, stream=stream)
     us = per_call_us(call, stream)
+    report("c1", us_per_call=round(us, 3), bound_us=TARGET_US)
     assert us <= TARGET_US, us
 
 
@@ -77,6 +86,7 @@ def test_c5_within_5us():
             arrms.ar_qknorm_run(plan, inp["shards"], wl.q_size, wl.kv_size, inp["q_weight"],
                                 inp["k_weight"], wl.eps, qo, ko, stream=stream)
     us = per_call_us(call, stream)
+    report("c5", us_per_call=round(us, 3), bound_us=TARGET_US)
     assert us <= TARGET_US, us
 
 
@@ -95,6 +105,7 @@ def test_c3_prefill_at_least_70_percent_of_peak():
         for _ in range(2):
             arrms.ar_rms_run(plan, inp["partials"], inp["residual"], inp["weight"], wl.eps,
                              False, norm, res, stream=stream)
-    us, _ = bench.graph_time(torch, call, 10, 2, 2, stream)
+    us = bench.graph_time(torch, call, 10, 2, 2, stream)
     frac = bench.rms_bytes(wl.W, T, wl.H) / (us * 1e-6) / (bench.HBM_PEAK_GBS * 1e9)
+    report("c3_T8192", us_per_call=round(us, 2), frac_of_peak=round(frac, 4), bound_frac=0.70)
     assert frac >= 0.70, (us, frac)
