@@ -173,23 +173,43 @@ def parse(argv=None):
 
 # ------------------------------------------------------------ GPU timing
 class Pool:
-    """One device allocation carved into 16-bit tensors at 4 KiB-aligned
-    offsets, so that many rotating input/output sets cost one allocation."""
+    """Rotating sets of 16-bit tensors in one device allocation: every set holds
+    the same shapes at the same 4 KiB-aligned offsets, one set after another."""
 
-    def __init__(self, torch, dev, nbytes, dtype):
-        self.torch = torch
-        self.buf = torch.empty(nbytes // 2 + 2048, dtype=dtype, device=dev)
-        self.off = 0
+    def __init__(self, torch, dev, shapes, n_sets, dtype):
+        self.shapes = list(shapes)
+        self.per_set = self.size_of(self.shapes)
+        self.n_sets = n_sets
+        self.buf = torch.empty(n_sets * self.per_set // 2, dtype=dtype, device=dev)
+        self.offsets = []
+        off = 0
+        for sh in self.shapes:
+            self.offsets.append(off)
+            off += self.span(sh)
 
     @staticmethod
-    def size_of(shapes):
-        return sum(-(-math.prod(s) * 2 // 4096) * 4096 for s in shapes)
+    def span(shape):
+        return -(-math.prod(shape) * 2 // 4096) * 4096
 
-    def take(self, shape):
-        n = math.prod(shape)
-        t = self.buf[self.off // 2: self.off // 2 + n].view(*shape)
-        self.off += -(-n * 2 // 4096) * 4096
-        return t
+    @classmethod
+    def size_of(cls, shapes):
+        return sum(cls.span(s) for s in shapes)
+
+    def tensor(self, s, i):
+        """Tensor i of set s."""
+        a = (s * self.per_set + self.offsets[i]) // 2
+        return self.buf[a: a + math.prod(self.shapes[i])].view(*self.shapes[i])
+
+    def sets(self, values):
+        """Copies `values` (one tensor per leading shape) into set 0, then set 0
+        into every other set with one broadcast copy; returns every set's
+        tensors."""
+        for i, v in enumerate(values):
+            self.tensor(0, i).copy_(v.reshape(self.shapes[i]))
+        rows = self.buf.view(self.n_sets, self.per_set // 2)
+        if self.n_sets > 1:
+            rows[1:].copy_(rows[:1].expand(self.n_sets - 1, -1))
+        return [[self.tensor(s, i) for i in range(len(self.shapes))] for s in range(self.n_sets)]
 
 
 def capture(torch, launch, stream):
@@ -294,22 +314,26 @@ def headline(torch, arrms, wl, cases, stream, args):
 def sweep_cold(torch, arrms, wl, cases, dev, stream, spg):
     """The sweep with its inputs and outputs rotated over sets that together
     hold more than 512 MiB (the values of every set are the sweep's own)."""
-    shapes = []
+    shapes, values = [], []
     for T, inp, *_ in cases:
         shapes += [(T, wl.H)] * (wl.W + 3)
+        values += inp["partials"] + [inp["residual"]]
+        values += [None, None]          # norm_out, residual_out: not filled
     per_set = Pool.size_of(shapes)
     n_sets = cold_sets(per_set, spg)
-    pool = Pool(torch, dev, per_set * n_sets, torch.bfloat16)
+    pool = Pool(torch, dev, shapes, n_sets, torch.bfloat16)
+    for i, v in enumerate(values):
+        if v is not None:
+            pool.tensor(0, i).copy_(v)
+    tensors = pool.sets([])
     sets = []
-    for _ in range(n_sets):
-        one = []
+    for st in tensors:
+        one, k = [], 0
         for T, inp, plan, norm, res in cases:
-            ps = [pool.take((T, wl.H)) for _ in range(wl.W)]
-            for d, s in zip(ps, inp["partials"]):
-                d.copy_(s)
-            r = pool.take((T, wl.H))
-            r.copy_(inp["residual"])
-            one.append((plan, ps, r, inp["weight"], pool.take((T, wl.H)), pool.take((T, wl.H))))
+            ps = st[k: k + wl.W]
+            one.append((plan, ps, st[k + wl.W], inp["weight"], st[k + wl.W + 1],
+                        st[k + wl.W + 2]))
+            k += wl.W + 3
         sets.append(one)
     torch.cuda.synchronize()
 
@@ -410,22 +434,17 @@ def time_rms(torch, arrms, wl, T, inp, plan, out, dev, stream):
         return r
     # cold: partials, residual and every output rotate; the weight is shared
     shapes = [(T, wl.H)] * (wl.W + 3)
-    per_set = Pool.size_of(shapes) + (Pool.size_of([(T, wl.H // 2)]) if wl.group else 0) \
-        + (Pool.size_of([(T, 2 * (wl.H // wl.group))]) if wl.group else 0)
-    n_sets = cold_sets(per_set, 100)
-    pool = Pool(torch, dev, per_set * n_sets, torch.bfloat16)
+    if wl.group:
+        shapes += [(T, wl.H // 2), (T, 2 * (wl.H // wl.group))]   # codes, scales
+    n_sets = cold_sets(Pool.size_of(shapes), 100)
+    pool = Pool(torch, dev, shapes, n_sets, torch.bfloat16)
     sets = []
-    for _ in range(n_sets):
-        ps = [pool.take((T, wl.H)) for _ in range(wl.W)]
-        for d, s in zip(ps, inp["partials"]):
-            d.copy_(s)
-        rr = pool.take((T, wl.H))
-        rr.copy_(inp["residual"])
-        o = {"norm": pool.take((T, wl.H)), "res": pool.take((T, wl.H))}
+    for st in pool.sets(inp["partials"] + [inp["residual"]]):
+        o = {"norm": st[wl.W + 1], "res": st[wl.W + 2]}
         if wl.group:
-            o["q"] = pool.take((T, wl.H // 2)).view(torch.uint8)
-            o["sc"] = pool.take((T, 2 * (wl.H // wl.group))).view(torch.float32)
-        sets.append((ps, rr, o))
+            o["q"] = st[wl.W + 3].view(torch.uint8)
+            o["sc"] = st[wl.W + 4].view(torch.float32)
+        sets.append((st[:wl.W], st[wl.W], o))
     torch.cuda.synchronize()
 
     def launch_set(s):
@@ -460,15 +479,9 @@ def time_qk(torch, arrms, workloads, wl, T, dev, stream):
     # cold: shards and outputs rotate through more than 512 MiB
     stride = wl.q_size + 2 * wl.kv_size
     shapes = [(T, stride)] * wl.W + [(wl.W, T, wl.q_size), (wl.W, T, wl.kv_size)]
-    per_set = Pool.size_of(shapes)
-    n_sets = cold_sets(per_set, 100)
-    pool = Pool(torch, dev, per_set * n_sets, torch.bfloat16)
-    sets = []
-    for _ in range(n_sets):
-        sh = [pool.take((T, stride)) for _ in range(wl.W)]
-        for d, s in zip(sh, inp["shards"]):
-            d.copy_(s)
-        sets.append((sh, pool.take((wl.W, T, wl.q_size)), pool.take((wl.W, T, wl.kv_size))))
+    n_sets = cold_sets(Pool.size_of(shapes), 100)
+    pool = Pool(torch, dev, shapes, n_sets, torch.bfloat16)
+    sets = [(st[:wl.W], st[wl.W], st[wl.W + 1]) for st in pool.sets(inp["shards"])]
     torch.cuda.synchronize()
 
     def launch_set(s):
@@ -603,8 +616,10 @@ def oracle_sweep(wl, cases):
 def main():
     args = parse()
     if args.check_args:
-        print(json.dumps(dict(step_plan(args), torch_imported="torch" in sys.modules)),
-              flush=True)
+        plan = step_plan(args)
+        for k in ("warmup_graphs", "timed_graphs"):   # {steps per graph: graphs}
+            plan[k] = {str(n): plan[k].count(n) for n in sorted(set(plan[k]), reverse=True)}
+        print(json.dumps(dict(plan, torch_imported="torch" in sys.modules)), flush=True)
         return
 
     import torch
@@ -644,18 +659,22 @@ def main():
     achieved = bytes_per_launch / (us_per_call * 1e-6) / 1e9
     log(f"[bench] {us_per_call:.3f} us/call over {calls} calls, {achieved:.1f} GB/s algorithmic")
 
-    traffic = rocprof_us = None
+    traffic = rocprof_us = rocprof_median = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
         if rec.get("kernel_source_sha") == kernel_source_sha():
             traffic = rec.get("traffic_bytes_per_launch")
             rocprof_us = rec.get("rocprof_mean_duration_us")
+            rocprof_median = rec.get("rocprof_median_duration_us")
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
                 "kernel": "reduce_norm_kernel<Bf16, W=4, 1 pack/lane, row-resident, residual>",
                 "bytes_per_launch": bytes_per_launch, "us_per_launch": round(us_per_call, 4),
                 "launches_timed": calls,
+                # the committed trace of the same headline: each dispatch alone on an
+                # otherwise idle GPU, so µs-scale durations differ from back-to-back calls
                 "rocprof_us_per_launch": rocprof_us,
+                "rocprof_median_us_per_launch": rocprof_median,
                 "rocprof_frac": (round(bytes_per_launch / (rocprof_us * 1e-6) / 1e9
                                        / HBM_PEAK_GBS, 5) if rocprof_us else None)}
 

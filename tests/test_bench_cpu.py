@@ -117,6 +117,11 @@ def run_bench(*argv):
                           capture_output=True, text=True, timeout=120)
 
 
+def steps_of(graphs):
+    """Steps covered by a {steps per graph: graphs} summary."""
+    return sum(int(n) * k for n, k in graphs.items())
+
+
 def test_driver_invocation_is_accepted_before_any_gpu_work():
     """The round-end command, `bench.py --gpus 1 --steps 20 --warmup 5`, with
     --check-args: the arguments pass, exactly 20 steps are timed after exactly
@@ -124,8 +129,8 @@ def test_driver_invocation_is_accepted_before_any_gpu_work():
     r = run_bench("--gpus", "1", "--steps", "20", "--warmup", "5", "--check-args")
     assert r.returncode == 0, r.stderr
     plan = json.loads(r.stdout)
-    assert plan["timed_steps"] == 20 and sum(plan["timed_graphs"]) == 20
-    assert plan["warmup_steps"] == 5 and sum(plan["warmup_graphs"]) == 5
+    assert plan["timed_steps"] == 20 and steps_of(plan["timed_graphs"]) == 20
+    assert plan["warmup_steps"] == 5 and steps_of(plan["warmup_graphs"]) == 5
     assert plan["torch_imported"] is False
 
 
@@ -133,7 +138,7 @@ def test_default_invocation_is_accepted():
     r = run_bench("--check-args")
     assert r.returncode == 0, r.stderr
     plan = json.loads(r.stdout)
-    assert sum(plan["timed_graphs"]) == plan["timed_steps"] >= 1
+    assert steps_of(plan["timed_graphs"]) == plan["timed_steps"] >= 1
 
 
 def test_bad_arguments_fail_fast_without_torch():
@@ -166,14 +171,23 @@ def test_cold_rotation_exceeds_the_caches():
                 assert n % calls == 0
 
 
-def test_pool_offsets_are_aligned_and_disjoint():
+def test_pool_sets_are_aligned_disjoint_and_replicated():
+    """The cold rotation's sets: every tensor 4 KiB-aligned within one
+    allocation, no two overlapping (within a set or across sets), and every set
+    holding the values copied into the first."""
     shapes = [(8, 1024), (3, 7), (80, 4096), (1, 8)]
-    sizes = [bench.Pool.size_of([s]) for s in shapes]
-    assert all(s % 4096 == 0 and s >= 2 * s_[0] * s_[1] for s, s_ in zip(sizes, shapes))
+    sizes = [bench.Pool.span(s) for s in shapes]
+    assert all(n % 4096 == 0 and n >= 2 * a * b for n, (a, b) in zip(sizes, shapes))
     assert bench.Pool.size_of(shapes) == sum(sizes)
-    p = bench.Pool(torch, "cpu", bench.Pool.size_of(shapes), torch.bfloat16)
-    ts = [p.take(s) for s in shapes]
-    spans = [(t.data_ptr(), t.data_ptr() + t.numel() * 2) for t in ts]
-    assert all(a % 4096 == spans[0][0] % 4096 for a, _ in spans)
+    p = bench.Pool(torch, "cpu", shapes, 3, torch.bfloat16)
+    vals = [torch.randn(s).to(torch.bfloat16) for s in shapes[:2]]
+    sets = p.sets(vals)
+    base = p.buf.data_ptr()
+    spans = sorted((t.data_ptr(), t.data_ptr() + t.numel() * 2) for st in sets for t in st)
+    assert all((a - base) % 4096 == 0 for a, _ in spans)
     assert all(spans[i][1] <= spans[i + 1][0] for i in range(len(spans) - 1))
-    assert spans[-1][1] <= p.buf.data_ptr() + p.buf.numel() * 2
+    assert spans[-1][1] <= base + p.buf.numel() * 2
+    for st in sets:
+        assert [tuple(x.shape) for x in st] == shapes
+        for x, v in zip(st, vals):
+            assert torch.equal(x, v)
