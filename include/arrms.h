@@ -23,8 +23,11 @@
  *    must be 16-byte aligned (every lane moves 16-byte packs of 8 elements).
  *  - Every call returns ARRMS_OK or a negative status and never returns OK
  *    without having queued the work that writes all requested outputs; on an
- *    error nothing is launched and no output is touched.  ar_rms_last_error()
- *    gives a message for the last non-OK status of the calling thread.
+ *    error nothing is launched and no output is touched.  This rules out the
+ *    failure the PR #54787 page warns about under "Risks and impact" item 1: an
+ *    older fused kernel that returned without writing its outputs.
+ *    ar_rms_last_error() gives a message for the last non-OK status of the
+ *    calling thread.
  *  - Work is queued on `stream` (a hipStream_t; NULL is the null stream) and is
  *    asynchronous; calls that overlap on their outputs race.
  *  - Results are deterministic: the same inputs give bit-identical outputs.
@@ -43,7 +46,11 @@ enum {
     ARRMS_OK = 0,
     ARRMS_EINVAL = -1,  /* malformed argument: null/misaligned pointer, bad size, bad eps */
     ARRMS_ENOTSUP = -2, /* well-formed but outside what the kernels cover: the caller
-                           falls back to the unfused path, as the pages' callers do */
+                           falls back to the unfused path, as the callers on the pages
+                           do (PR #54787 page, "Key source excerpts": the all_reduce +
+                           norm branch of fused_allreduce_gemma_rms_norm; PR #44849
+                           page, "Key source excerpts": the final fallback of
+                           _minimax_qk_norm_fusion) */
     ARRMS_EHIP = -3,    /* the HIP runtime refused the launch */
     ARRMS_ENOMEM = -4   /* host memory for a plan could not be allocated */
 };

@@ -37,7 +37,8 @@
 //              its registers leave room for two workgroups per CU.
 // The looping bodies stream partials and residual with non-temporal loads
 // (read once); the weight row is loaded once per workgroup and kept in
-// registers (split-wide reloads it per row from L2).
+// registers (split-wide with one pack per lane keeps it in LDS; with four,
+// reloads it per row from L2).
 //
 // There is no inter-workgroup communication, no atomics and no scratch
 // memory: every output is a fixed function of the inputs and bit-identical
@@ -300,9 +301,16 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     // kSplit: `ahead` receives the next row's loads one row in advance
     u32x4 ahead[PPL][NB];
     if constexpr (MODE == kSplit) load_row<W, PPL, RES, MODE != kRow>(p, row, tid, nthr, ahead);
-    // weight row: loaded once per workgroup and kept (kSplitWide reloads it
-    // per row from L2 after the row's reduction, to stay within registers);
-    // converted where used, so no wait on it stands before the row's loads
+    // weight row: loaded once per workgroup and kept in registers.  The
+    // split-wide bodies have none to spare: with one pack per lane they keep it
+    // in LDS (each lane its own pack, written once), so that nothing after a
+    // row's reduction waits on vector memory (a reload from L2 there waited
+    // for it and for the row's residual_out stores: measured 1-1.5 % slower);
+    // with several packs per lane they reload it per row from L2 after the
+    // row's reduction.  Converted where used, so no wait on it stands before
+    // the row's loads.
+    constexpr bool kWeightLds = MODE == kSplitWide && PPL == 1;
+    __shared__ u32x4 weight_lds[kWeightLds ? kMaxBlock : 1];
     u32x4 wraw[PPL];
     auto load_weight = [&]() {
 #pragma unroll
@@ -311,7 +319,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
             wraw[k] = load16(p.weight + size_t(pk < p.packs ? pk : 0) * 16);
         }
     };
-    if constexpr (MODE != kSplitWide) load_weight();
+    if constexpr (MODE != kSplitWide || kWeightLds) load_weight();
 
     // 1/H for the FP8 variant, formed while the row's loads are in flight: its
     // epilogue's dependent chain is long enough that the division after the
@@ -330,6 +338,10 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
         } else {
             load_row<W, PPL, RES, MODE != kRow>(p, row, tid, nthr, cur);
         }
+        // the first row's loads are out: the weight pack (loaded before them)
+        // goes to LDS
+        if constexpr (kWeightLds)
+            if (row == int64_t(blockIdx.x)) weight_lds[tid] = wraw[0];
         // keeps the compiler from moving the division next to its use
         if constexpr (QUANT) asm volatile("" : "+v"(inv_h));
         const size_t base = size_t(row) * size_t(p.H) * 2;
@@ -393,7 +405,8 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
         const float rstd = rsqrtf((QUANT ? total * inv_h : total / float(p.H)) + p.eps);
 
         // phase 2: normalise, weight, store; optional FP8 group epilogue
-        if constexpr (MODE == kSplitWide) load_weight();
+        if constexpr (kWeightLds) wraw[0] = weight_lds[tid];
+        else if constexpr (MODE == kSplitWide) load_weight();
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
             const int pk = tid + k * nthr;
