@@ -98,6 +98,15 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
         if (lean.launch && lean_resident >= 2 * resident) {
             v = lean;
             grid = grid < lean_resident ? grid : lean_resident;
+            // With at most two rows per workgroup a workgroup's stores gather at
+            // the end of the call; streaming residual_out as well as norm_out
+            // then measured 1-3.4 % faster cold at W = 8 (T = 768, 1024), and
+            // 1.6-2.4 % slower with three or four rows per workgroup.
+            if (plan->T <= 2 * grid) {
+                const Variant stream_res =
+                    pick_rms(plan->dtype, plan->W, kSplitLeanStream, quant, res, round);
+                if (stream_res.launch) v = stream_res;
+            }
         } else if (grid > resident) {
             grid = resident;
         } else if (mode == kSplit) {

@@ -309,7 +309,8 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     // with several packs per lane they reload it per row from L2 after the
     // row's reduction.  Converted where used, so no wait on it stands before
     // the row's loads.
-    constexpr bool kWeightLds = MODE == kSplitWide && PPL == 1;
+    constexpr bool kWide = MODE == kSplitWide || MODE == kSplitLeanStream;
+    constexpr bool kWeightLds = kWide && PPL == 1;
     __shared__ u32x4 weight_lds[kWeightLds ? kMaxBlock : 1];
     u32x4 wraw[PPL];
     auto load_weight = [&]() {
@@ -319,7 +320,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
             wraw[k] = load16(p.weight + size_t(pk < p.packs ? pk : 0) * 16);
         }
     };
-    if constexpr (MODE != kSplitWide || kWeightLds) load_weight();
+    if constexpr (!kWide || kWeightLds) load_weight();
 
     // 1/H for the FP8 variant, formed while the row's loads are in flight: its
     // epilogue's dependent chain is long enough that the division after the
@@ -381,7 +382,14 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
                     store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
             } else {
                 if (pk < p.packs) {
-                    if (p.residual_out) store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
+                    if (p.residual_out) {
+                        // kSplitLeanStream (at most two rows per workgroup):
+                        // both outputs stream; see run_rms
+                        if constexpr (MODE == kSplitLeanStream)
+                            store16_stream(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
+                        else
+                            store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
+                    }
                 } else {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) acc[k][i] = 0.0f;
@@ -406,7 +414,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
 
         // phase 2: normalise, weight, store; optional FP8 group epilogue
         if constexpr (kWeightLds) wraw[0] = weight_lds[tid];
-        else if constexpr (MODE == kSplitWide) load_weight();
+        else if constexpr (kWide) load_weight();
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
             const int pk = tid + k * nthr;
@@ -737,8 +745,8 @@ Variant variant() {
 
 // Modes built: kRow and kSplit with one pack per lane, kSplitWide with four
 // packs per lane (rows longer than 8192 elements), kSplitLean (the kSplitWide
-// body with one pack per lane) for four to eight partials without the FP8
-// epilogue.
+// body with one pack per lane) and kSplitLeanStream (the same, residual_out
+// streamed too) for four to eight partials without the FP8 epilogue.
 template <typename IO, int W, bool QUANT, bool RES, bool ROUND>
 Variant pick_mode(int mode) {
     switch (mode) {
@@ -747,6 +755,10 @@ Variant pick_mode(int mode) {
     case kSplitWide: return variant<IO, W, kMaxPpl, kSplitWide, QUANT, RES, ROUND>();
     case kSplitLean:
         if constexpr (!QUANT && W >= 4) return variant<IO, W, 1, kSplitWide, QUANT, RES, ROUND>();
+        return Variant{nullptr, nullptr};
+    case kSplitLeanStream:
+        if constexpr (!QUANT && W >= 4)
+            return variant<IO, W, 1, kSplitLeanStream, QUANT, RES, ROUND>();
         return Variant{nullptr, nullptr};
     default: return Variant{nullptr, nullptr};
     }
