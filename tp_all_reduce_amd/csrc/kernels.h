@@ -36,9 +36,12 @@
 //              lean mode), for split plans of only a few rows per workgroup:
 //              its registers leave room for two workgroups per CU.
 // The looping bodies stream partials and residual with non-temporal loads
-// (read once); the weight row is loaded once per workgroup and kept in
-// registers (split-wide with one pack per lane keeps it in LDS; with four,
-// reloads it per row from L2).
+// (read once) and store norm_out with the non-temporal hint; residual_out,
+// next read a layer later, is stored with it by the bodies that store at the
+// end of the call (row, and lean with at most two rows per workgroup).  The
+// weight row is loaded once per workgroup and kept in registers (split-wide
+// with one pack per lane keeps it in LDS; with four, reloads it per row from
+// L2).
 //
 // There is no inter-workgroup communication, no atomics and no scratch
 // memory: every output is a fixed function of the inputs and bit-identical
@@ -310,6 +313,13 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     // row's reduction.  Converted where used, so no wait on it stands before
     // the row's loads.
     constexpr bool kWide = MODE == kSplitWide || MODE == kSplitLeanStream;
+    // residual_out is next read a whole layer later, so bodies that issue
+    // their stores at the end of the call stream it past the caches: the row
+    // body (c4 warm 4.45 -> 4.02 us, cold and decode unchanged or faster) and
+    // the lean body with at most two rows per workgroup (see run_rms); the
+    // looping bodies keep it cached (mixed, up to 7 % slower there).  norm_out
+    // is read next by the following layer's GEMM: the row body keeps it cached.
+    constexpr bool kStreamResidual = MODE == kRow || MODE == kSplitLeanStream;
     constexpr bool kWeightLds = kWide && PPL == 1;
     __shared__ u32x4 weight_lds[kWeightLds ? kMaxBlock : 1];
     u32x4 wraw[PPL];
@@ -378,14 +388,16 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(acc[k][i], acc[k][i], ss);
-                if (pk < p.packs && p.residual_out)
-                    store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
+                if (pk < p.packs && p.residual_out) {
+                    if constexpr (kStreamResidual)
+                        store16_stream(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
+                    else
+                        store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
+                }
             } else {
                 if (pk < p.packs) {
                     if (p.residual_out) {
-                        // kSplitLeanStream (at most two rows per workgroup):
-                        // both outputs stream; see run_rms
-                        if constexpr (MODE == kSplitLeanStream)
+                        if constexpr (kStreamResidual)
                             store16_stream(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
                         else
                             store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
