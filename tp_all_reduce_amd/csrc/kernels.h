@@ -304,14 +304,7 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     // kSplit: `ahead` receives the next row's loads one row in advance
     u32x4 ahead[PPL][NB];
     if constexpr (MODE == kSplit) load_row<W, PPL, RES, MODE != kRow>(p, row, tid, nthr, ahead);
-    // weight row: loaded once per workgroup and kept in registers.  The
-    // split-wide bodies have none to spare: with one pack per lane they keep it
-    // in LDS (each lane its own pack, written once), so that nothing after a
-    // row's reduction waits on vector memory (a reload from L2 there waited
-    // for it and for the row's residual_out stores: measured 1-1.5 % slower);
-    // with several packs per lane they reload it per row from L2 after the
-    // row's reduction.  Converted where used, so no wait on it stands before
-    // the row's loads.
+    // kSplitLeanStream is the kSplitWide body with one more store hint
     constexpr bool kWide = MODE == kSplitWide || MODE == kSplitLeanStream;
     // residual_out is next read a whole layer later, so bodies that issue
     // their stores at the end of the call stream it past the caches: the row
@@ -320,6 +313,14 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     // looping bodies keep it cached (mixed, up to 7 % slower there).  norm_out
     // is read next by the following layer's GEMM: the row body keeps it cached.
     constexpr bool kStreamResidual = MODE == kRow || MODE == kSplitLeanStream;
+    // weight row: loaded once per workgroup and kept in registers.  The
+    // split-wide bodies have none to spare: with one pack per lane they keep it
+    // in LDS (each lane its own pack, written once), so that nothing after a
+    // row's reduction waits on vector memory (a reload from L2 there waited
+    // for it and for the row's residual_out stores: measured 1-1.5 % slower);
+    // with several packs per lane they reload it per row from L2 after the
+    // row's reduction.  Converted where used, so no wait on it stands before
+    // the row's loads.
     constexpr bool kWeightLds = kWide && PPL == 1;
     __shared__ u32x4 weight_lds[kWeightLds ? kMaxBlock : 1];
     u32x4 wraw[PPL];
