@@ -122,10 +122,11 @@ def steps_of(graphs):
     return sum(int(n) * k for n, k in graphs.items())
 
 
-def test_driver_invocation_is_accepted_before_any_gpu_work():
-    """The round-end command, `bench.py --gpus 1 --steps 20 --warmup 5`, with
-    --check-args: the arguments pass, exactly 20 steps are timed after exactly
-    5 warm-up steps, and torch has not been imported by then."""
+def test_short_invocation_is_accepted_before_any_gpu_work():
+    """`bench.py --gpus 1 --steps 20 --warmup 5 --check-args` (step counts that
+    are not multiples of the steps per graph): the arguments pass, exactly 20
+    steps are timed after exactly 5 warm-up steps, and torch has not been
+    imported by then."""
     r = run_bench("--gpus", "1", "--steps", "20", "--warmup", "5", "--check-args")
     assert r.returncode == 0, r.stderr
     plan = json.loads(r.stdout)
