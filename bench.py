@@ -682,7 +682,13 @@ def main():
                           "T in {1,2,4,8,16,21,22,32,64,80}, row-resident kernel; one step = 10 "
                           "fused calls, graph-replayed",
               "io_dtype": "bf16", "W": W, "H": H, "T": list(Ts), "calls_per_step": len(Ts),
-              "steps_per_graph": spg, "timed_graphs": len(plan["timed_graphs"])}
+              "steps_per_graph": spg, "timed_graphs": len(plan["timed_graphs"]),
+              # the default dispatch per T (the one-stage window predicate): the
+              # sweep forces the row-resident kernel throughout; beyond the
+              # window a default plan is a split plan, whose grid of one
+              # workgroup per row runs the same row body at these sizes
+              "default_plan_kernel": {str(T): ("row" if arrms.cached_plan(W, T, H, arrms.BF16).kernel
+                                               == arrms.KERNEL_ROW else "split") for T in Ts}}
 
     if not args.headline_only:
         log("[bench] the sweep with rotated inputs (cold) and as a dependent chain")
