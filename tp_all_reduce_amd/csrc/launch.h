@@ -84,10 +84,10 @@ struct Variant {
     const void *symbol;
 };
 
-// Reduce + RMSNorm variant for W partials, mode (kRow / kSplit / kSplitWide),
-// a residual term or none, and the reduced sum rounded to the I/O format or
-// not; {nullptr, nullptr} when no such kernel is built.  One function per I/O
-// format (bf16, fp16) and epilogue (none, FP8 group quant).
+// Reduce + RMSNorm variant for W partials, mode (a Mode above), a residual
+// term or none, and the reduced sum rounded to the I/O format or not;
+// {nullptr, nullptr} when no such kernel is built.  One function per I/O format
+// (bf16, fp16) and epilogue (none, FP8 group quant).
 Variant pick_rms_bf16(int W, int mode, bool res, bool round);
 Variant pick_rms_bf16_fp8(int W, int mode, bool res, bool round);
 Variant pick_rms_fp16(int W, int mode, bool res, bool round);
