@@ -251,3 +251,31 @@ def test_binding_device_and_stream_checks():
         arrms._stream(FakeStream(), torch.device("cuda", 0))
     assert arrms._stream(FakeStream(), torch.device("cuda", 1)) == 0
     assert arrms._stream(1234) == 1234
+
+
+def test_plan_cache_is_bounded_and_held_plans_stay_valid(monkeypatch):
+    monkeypatch.setattr(arrms, "PLAN_CACHE_MAX", 4)
+    monkeypatch.setattr(arrms, "_plans", arrms.OrderedDict())
+    first = arrms.cached_plan(2, 1, 1024, arrms.BF16)
+    assert arrms.cached_plan(2, 1, 1024, arrms.BF16) is first
+    for T in range(2, 12):
+        arrms.cached_plan(2, T, 1024, arrms.BF16)
+    assert len(arrms._plans) == 4
+    assert list(arrms._plans)[-1] == (2, 11, 1024, arrms.BF16, 0)
+    # evicted from the cache, still usable through the caller's reference
+    assert (2, 1, 1024, arrms.BF16, 0) not in arrms._plans
+    assert first.kernel == arrms.KERNEL_ROW
+    # a hit moves the entry to the most recent end
+    arrms.cached_plan(2, 8, 1024, arrms.BF16)
+    assert list(arrms._plans)[-1] == (2, 8, 1024, arrms.BF16, 0)
+
+
+def test_fused_helpers_take_only_new_none_or_a_tensor_for_residual_out():
+    import torch
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="residual_out"):
+        arrms._new_residual_out("alloc", x, x)
+    assert arrms._new_residual_out(None, x, x) is None
+    assert arrms._new_residual_out(x, x, x) is x
+    y = arrms._new_residual_out("new", None, x)
+    assert y.shape == x.shape and y.dtype == x.dtype

@@ -17,6 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
+from collections import OrderedDict
 
 import torch
 
@@ -236,16 +237,40 @@ def ar_qknorm_run(plan: Plan, qkv, q_size: int, kv_size: int, q_weight, k_weight
 
 
 # ------------------------------------------------------ tensor-level helpers
-_plans: dict = {}
+PLAN_CACHE_MAX = 1024
+_plans: OrderedDict = OrderedDict()
+_plans_lock = threading.Lock()
 
 
 def cached_plan(W: int, T: int, H: int, dtype: int, flags: int = 0) -> Plan:
-    """Plans depend only on (W, T, H, dtype, flags), so they are shared."""
-    key = (W, T, H, dtype, flags)
-    p = _plans.get(key)
-    if p is None:
-        p = _plans[key] = Plan(W, T, H, dtype, flags)
+    """Plans depend only on (W, T, H, dtype, flags), so they are shared.  The
+    PLAN_CACHE_MAX most recently used are kept (a serving loop meets many
+    token counts); a plan still held by a caller stays valid after it leaves
+    the cache, since it is destroyed only with its last reference."""
+    key = (int(W), int(T), int(H), int(dtype), int(flags))
+    with _plans_lock:
+        p = _plans.get(key)
+        if p is not None:
+            _plans.move_to_end(key)
+            return p
+    p = Plan(W, T, H, dtype, flags)
+    with _plans_lock:
+        p = _plans.setdefault(key, p)
+        _plans.move_to_end(key)
+        while len(_plans) > PLAN_CACHE_MAX:
+            _plans.popitem(last=False)
     return p
+
+
+def _new_residual_out(residual_out, residual, x):
+    """residual_out as the fused_* helpers take it: "new" allocates it shaped
+    like the residual (like the first partial without one); None or a tensor
+    passes through."""
+    if isinstance(residual_out, str):
+        if residual_out != "new":
+            raise ValueError(f'residual_out: "new", None or a tensor, got {residual_out!r}')
+        return torch.empty_like(residual if residual is not None else x)
+    return residual_out
 
 
 def _tokens(x: torch.Tensor) -> tuple[int, int]:
@@ -266,8 +291,7 @@ def fused_allreduce_rms_norm(partials, residual, weight, eps: float, gemma: bool
     dtype = _CODE_OF[x.dtype]
     plan = cached_plan(len(partials), T, H, dtype, flags)
     norm_out = torch.empty_like(x)
-    if isinstance(residual_out, str):
-        residual_out = torch.empty_like(residual if residual is not None else x)
+    residual_out = _new_residual_out(residual_out, residual, x)
     ar_rms_run(plan, partials, residual, weight, eps, gemma, norm_out, residual_out, stream)
     return norm_out, residual_out
 
@@ -287,8 +311,7 @@ def fused_allreduce_rms_norm_quant(partials, residual, weight, eps: float, group
     q_out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     scales = torch.empty((*x.shape[:-1], H // group_size if group_size > 0 else 0),
                          dtype=torch.float32, device=x.device)
-    if isinstance(residual_out, str):
-        residual_out = torch.empty_like(residual if residual is not None else x)
+    residual_out = _new_residual_out(residual_out, residual, x)
     ar_rms_quant_run(plan, partials, residual, weight, eps, gemma, group_size, norm_out, q_out,
                      scales, residual_out, stream)
     return norm_out, q_out, scales, residual_out
