@@ -168,11 +168,11 @@ int ar_rms_quant_run(const ar_rms_plan_s *plan, const void *const *partials,
  *   qkv        host array of W device pointers, each [T, q_size + 2*kv_size]
  *   q_weight   device [W * q_size];  k_weight  device [W * kv_size]
  *   q_out      device [W, T, q_size];  k_out  device [W, T, kv_size]
- * ENOTSUP unless q_size and kv_size are positive multiples of 256 (32 lanes of
- * 16-byte packs: the alignment the fused QK kernel requires, PR #44849 page,
- * "Implementation breakdown" item 3) with q_size + 2 * kv_size == H and
- * W * (q_size + kv_size) <= 32768, and unless W <= 8; the plan's FORCE flags
- * do not apply.
+ * EINVAL if q_size or kv_size is not positive; ENOTSUP unless both are
+ * multiples of 256 (32 lanes of 16-byte packs: the alignment the fused QK
+ * kernel requires, PR #44849 page, "Implementation breakdown" item 3) with
+ * q_size + 2 * kv_size == H and W * (q_size + kv_size) <= 32768, and unless
+ * W <= 8; the plan's FORCE flags do not apply.
  */
 int ar_qknorm_run(const ar_rms_plan_s *plan, const void *const *qkv, int q_size, int kv_size,
                   const void *q_weight, const void *k_weight, float eps, void *q_out,
