@@ -99,13 +99,13 @@ int run_rms(const ar_rms_plan_s *plan, const void *const *partials, const void *
             v = lean;
             grid = grid < lean_resident ? grid : lean_resident;
             // With at most two rows per workgroup a workgroup's stores gather at
-            // the end of the call; streaming residual_out as well as norm_out
-            // then measured 1-3.4 % faster cold at W = 8 (T = 768, 1024), and
-            // 1.6-2.4 % slower with three or four rows per workgroup.
+            // the end of the call, and norm_out stored at device scope measured
+            // 2-3 % slower there (eight partials, 512 and 1024 rows): those
+            // plans take the body whose norm_out stores are only non-temporal.
             if (plan->T <= 2 * grid) {
-                const Variant stream_res =
-                    pick_rms(plan->dtype, plan->W, kSplitLeanStream, quant, res, round);
-                if (stream_res.launch) v = stream_res;
+                const Variant few =
+                    pick_rms(plan->dtype, plan->W, kSplitLeanFew, quant, res, round);
+                if (few.launch) v = few;
             }
         } else if (grid > resident) {
             grid = resident;

@@ -36,9 +36,9 @@
 //              lean mode), for split plans of only a few rows per workgroup:
 //              its registers leave room for two workgroups per CU.
 // The looping bodies stream partials and residual with non-temporal loads
-// (read once) and store norm_out with the non-temporal hint; residual_out,
-// next read a layer later, is stored with it by the bodies that store at the
-// end of the call (row, and lean with at most two rows per workgroup).  The
+// (read once) and write their outputs at device scope, through the XCDs' L2
+// caches; the row body stores residual_out, next read a layer later, with the
+// non-temporal hint (reduce_norm states the store policy of each body).  The
 // weight row is loaded once per workgroup and kept in registers (split-wide
 // with one pack per lane keeps it in LDS; with four, reloads it per row from
 // L2).
@@ -126,6 +126,40 @@ __device__ __forceinline__ void store16(uint8_t *p, u32x4 v) {
 // Streaming store (non-temporal hint).
 __device__ __forceinline__ void store16_stream(uint8_t *p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
+// Cache policy of an output store, as the bits of the cache-policy operand of
+// a gfx950 buffer store: bit 1 the non-temporal hint, bit 4 device scope (the
+// store is written through the XCD's L2 rather than left there dirty, to be
+// written back when it is evicted or when the kernel ends).
+enum StorePolicy {
+    kStorePlain = 0,
+    kStoreStream = 2,
+    kStoreDevice = 16,
+    kStoreDeviceStream = 16 | 2,
+};
+
+// Word 3 of a raw buffer resource: 32-bit data format, the setting untyped
+// buffer accesses expect on gfx9-family GPUs.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// 16-byte store of one lane's pack at `off` bytes past a wave-uniform `base`
+// (a row of `bytes` bytes) with the given cache policy.  Plain and
+// non-temporal stores are global stores; the device-scope ones are buffer
+// stores, whose resource (in scalar registers) holds the row's base and
+// length, so a store past the row would be dropped by the hardware.
+template <int POLICY>
+__device__ __forceinline__ void store16_policy(uint8_t *base, uint32_t off, uint32_t bytes,
+                                               u32x4 v) {
+    if constexpr (POLICY == kStorePlain) {
+        store16(base + off, v);
+    } else if constexpr (POLICY == kStoreStream) {
+        store16_stream(base + off, v);
+    } else {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), kRawBufferWord3);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, POLICY);
+    }
 }
 
 // ---------------------------------------------------------------- wave64 ops
@@ -304,15 +338,27 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     // kSplit: `ahead` receives the next row's loads one row in advance
     u32x4 ahead[PPL][NB];
     if constexpr (MODE == kSplit) load_row<W, PPL, RES, MODE != kRow>(p, row, tid, nthr, ahead);
-    // kSplitLeanStream is the kSplitWide body with one more store hint
-    constexpr bool kWide = MODE == kSplitWide || MODE == kSplitLeanStream;
-    // residual_out is next read a whole layer later, so bodies that issue
-    // their stores at the end of the call stream it past the caches: the row
-    // body (c4 warm 4.45 -> 4.02 us, cold and decode unchanged or faster) and
-    // the lean body with at most two rows per workgroup (see run_rms); the
-    // looping bodies keep it cached (mixed, up to 7 % slower there).  norm_out
-    // is read next by the following layer's GEMM: the row body keeps it cached.
-    constexpr bool kStreamResidual = MODE == kRow || MODE == kSplitLeanStream;
+    // kSplitLeanFew is the kSplitWide body with another store policy
+    constexpr bool kWide = MODE == kSplitWide || MODE == kSplitLeanFew;
+    // Store policies of residual_out and norm_out, per body, as measured
+    // (back-to-back calls, inputs resident in HBM and in the caches):
+    //  - looping bodies: both at device scope, norm_out also non-temporal
+    //    (1-3 % faster than write-back stores from 2048 rows on, 8192 rows
+    //    of eight partials 238.4 -> 233.2 us);
+    //  - lean body with at most two rows per workgroup: residual_out at
+    //    device scope, norm_out only non-temporal (device scope on norm_out
+    //    measured 2-3 % slower there; 1024 rows 32.7 -> 32.55 us);
+    //  - row body: residual_out non-temporal (it is next read a layer later;
+    //    the FP8 call 4.45 -> 4.02 us), norm_out write-back where the next
+    //    layer's GEMM reads it at once, or at device scope with the FP8
+    //    epilogue (256 rows of 7168: 4.03 -> 3.69 us; device scope on the
+    //    plain row body's stores measured up to 8 % slower on the smallest
+    //    calls).
+    constexpr int kResidualPolicy = MODE == kRow ? kStoreStream : kStoreDevice;
+    constexpr int kNormPolicy = MODE == kRow        ? (QUANT ? kStoreDevice : kStorePlain)
+                                : MODE == kSplitLeanFew ? kStoreStream
+                                                        : kStoreDeviceStream;
+    const uint32_t row_bytes = uint32_t(p.packs) * 16;
     // weight row: loaded once per workgroup and kept in registers.  The
     // split-wide bodies have none to spare: with one pack per lane they keep it
     // in LDS (each lane its own pack, written once), so that nothing after a
@@ -389,20 +435,14 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(acc[k][i], acc[k][i], ss);
-                if (pk < p.packs && p.residual_out) {
-                    if constexpr (kStreamResidual)
-                        store16_stream(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
-                    else
-                        store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
-                }
+                if (pk < p.packs && p.residual_out)
+                    store16_policy<kResidualPolicy>(p.residual_out + base, uint32_t(pk) * 16,
+                                                    row_bytes, pack8<IO>(acc[k]));
             } else {
                 if (pk < p.packs) {
-                    if (p.residual_out) {
-                        if constexpr (kStreamResidual)
-                            store16_stream(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
-                        else
-                            store16(p.residual_out + base + size_t(pk) * 16, pack8<IO>(acc[k]));
-                    }
+                    if (p.residual_out)
+                        store16_policy<kResidualPolicy>(p.residual_out + base, uint32_t(pk) * 16,
+                                                        row_bytes, pack8<IO>(acc[k]));
                 } else {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) acc[k][i] = 0.0f;
@@ -441,15 +481,9 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
             float y[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] = (acc[k][i] * rstd) * w[i];
-            if (valid && p.norm_out) {
-                // Large-T modes stream norm_out past the caches: measured faster
-                // at every prefill size (most at 16384 rows); the same hint on
-                // residual_out as well lost 5 % at 8192 rows.
-                if constexpr (MODE == kRow)
-                    store16(p.norm_out + base + size_t(pk) * 16, pack8<IO>(y));
-                else
-                    store16_stream(p.norm_out + base + size_t(pk) * 16, pack8<IO>(y));
-            }
+            if (valid && p.norm_out)
+                store16_policy<kNormPolicy>(p.norm_out + base, uint32_t(pk) * 16, row_bytes,
+                                            pack8<IO>(y));
             if constexpr (QUANT) {
                 float amax = 0.0f;
 #pragma unroll
@@ -758,8 +792,9 @@ Variant variant() {
 
 // Modes built: kRow and kSplit with one pack per lane, kSplitWide with four
 // packs per lane (rows longer than 8192 elements), kSplitLean (the kSplitWide
-// body with one pack per lane) and kSplitLeanStream (the same, residual_out
-// streamed too) for four to eight partials without the FP8 epilogue.
+// body with one pack per lane) and kSplitLeanFew (the same with the store
+// policy for at most two rows per workgroup) for four to eight partials
+// without the FP8 epilogue.
 template <typename IO, int W, bool QUANT, bool RES, bool ROUND>
 Variant pick_mode(int mode) {
     switch (mode) {
@@ -769,9 +804,9 @@ Variant pick_mode(int mode) {
     case kSplitLean:
         if constexpr (!QUANT && W >= 4) return variant<IO, W, 1, kSplitWide, QUANT, RES, ROUND>();
         return Variant{nullptr, nullptr};
-    case kSplitLeanStream:
+    case kSplitLeanFew:
         if constexpr (!QUANT && W >= 4)
-            return variant<IO, W, 1, kSplitLeanStream, QUANT, RES, ROUND>();
+            return variant<IO, W, 1, kSplitLeanFew, QUANT, RES, ROUND>();
         return Variant{nullptr, nullptr};
     default: return Variant{nullptr, nullptr};
     }

@@ -52,10 +52,9 @@ constexpr int32_t kGemma = 1;         // weight applied as 1 + w (Gemma RMSNorm)
 // partials.  kSplitLean: the kSplitWide body with one pack per lane for four to
 // eight partials without the FP8 epilogue; it needs few enough registers for
 // two workgroups per CU, which beats the row-ahead loads when each workgroup
-// would get only a few rows.  kSplitLeanStream: the same body storing
-// residual_out with the non-temporal hint too, for at most two rows per
-// workgroup.
-enum Mode { kRow = 0, kSplit = 1, kSplitWide = 2, kSplitLean = 3, kSplitLeanStream = 4 };
+// would get only a few rows.  kSplitLeanFew: the same body with the store
+// policy for at most two rows per workgroup (norm_out without device scope).
+enum Mode { kRow = 0, kSplit = 1, kSplitWide = 2, kSplitLean = 3, kSplitLeanFew = 4 };
 
 // ------------------------------------------------------------- QK-norm
 struct QkParams {
