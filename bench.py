@@ -228,15 +228,21 @@ def capture(torch, launch, stream):
 
 
 def replay_timed(torch, stream, warm, timed):
-    """Replays the graphs `warm` (untimed), then `timed` between two device
-    synchronisations; returns the elapsed ms of the timed replays measured with
-    HIP events on `stream`, the stream they are replayed on."""
+    """Replays the graphs `warm` (untimed), then `timed`; returns the elapsed ms
+    of the timed replays measured with HIP events on `stream`, the stream they
+    are replayed on.  The device is synchronised before the last warm-up replay
+    and after the timed ones.  That last warm-up replay is still running when
+    the start event and the timed replays are queued, so the timed region opens
+    on a queued kernel and does not include the host's launch of the first
+    timed graph (with no warm-up graph it does)."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        for g in warm:
+        for g in warm[:-1]:
             g.replay()
         torch.cuda.synchronize()
+        if warm:
+            warm[-1].replay()
         start.record(stream)
         for g in timed:
             g.replay()
