@@ -355,9 +355,9 @@ __device__ __forceinline__ void reduce_norm(const RmsParams &p) {
     //    plain row body's stores measured up to 8 % slower on the smallest
     //    calls).
     constexpr int kResidualPolicy = MODE == kRow ? kStoreStream : kStoreDevice;
-    constexpr int kNormPolicy = MODE == kRow        ? (QUANT ? kStoreDevice : kStorePlain)
-                                : MODE == kSplitLeanFew ? kStoreStream
-                                                        : kStoreDeviceStream;
+    constexpr int kNormPolicy = MODE == kRow ? (QUANT ? kStoreDevice : kStorePlain)
+                              : MODE == kSplitLeanFew ? kStoreStream
+                              : kStoreDeviceStream;
     const uint32_t row_bytes = uint32_t(p.packs) * 16;
     // weight row: loaded once per workgroup and kept in registers.  The
     // split-wide bodies have none to spare: with one pack per lane they keep it
