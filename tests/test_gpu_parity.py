@@ -599,8 +599,8 @@ def test_split_band_of_few_rows_per_workgroup(W, form, dtype):
     partials without the FP8 epilogue may run on twice the workgroups per CU
     without the row-ahead loads: every form of the call at rows of 8192 (one
     workgroup per CU otherwise) and 4096 elements, with at most two rows per
-    workgroup (residual_out streamed too: T = 700 and 1024 at 8192 elements,
-    1100 at 4096) and with more (T = 1500 at 8192, 2500 at 4096)."""
+    workgroup (the body with the few-rows store policy: T = 700 and 1024 at 8192
+    elements, 1100 at 4096) and with more (T = 1500 at 8192, 2500 at 4096)."""
     fmt = FMT[dtype]
     for H, T in ((8192, 700), (8192, 1024), (8192, 1500), (4096, 1100), (4096, 2500)):
         inp = cuda_inputs(WORKLOADS["c3"], T, dtype, W=W, H=H, seed=W * 100 + T,
