@@ -380,6 +380,49 @@ def test_deterministic_and_row_split_agree():
     assert torch.equal(a[1].view(torch.int16), s1[1].view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("gemma", [False, True], ids=["standard", "gemma"])
+def test_kernel_bodies_agree_bit_for_bit(gemma, dtype):
+    """With one pack per lane every body adds and reduces in the same order, so
+    a row's outputs do not depend on which body ran it: the row-ahead loop
+    (5000 rows), the lean body (1500), the lean body of few rows per workgroup
+    (700), the row body behind a split plan (200) and the row-resident plan
+    (64) give the same bits for the rows they share, whatever their store
+    policies.  Same for the FP8 epilogue: the row-ahead loop (2048 rows)
+    against the row body (256)."""
+    inp = cuda_inputs(GENERIC, 5000, dtype, W=8, H=8192, seed=4242, device_draw=True)
+    full = run_rms(inp, 1e-5, gemma)
+    outs = {}
+    for n, flags in ((1500, 0), (700, 0), (200, 0), (64, arrms.FORCE_ROW)):
+        part = {"partials": [p[:n] for p in inp["partials"]], "residual": inp["residual"][:n],
+                "weight": inp["weight"]}
+        outs[n] = run_rms(part, 1e-5, gemma, flags=flags)
+    torch.cuda.synchronize()
+    for n, (norm, res) in outs.items():
+        assert torch.equal(norm.view(torch.int16), full[0][:n].view(torch.int16)), n
+        assert torch.equal(res.view(torch.int16), full[1][:n].view(torch.int16)), n
+    del inp, full, outs
+
+    qinp = cuda_inputs(WORKLOADS["c4"], 2048, dtype, seed=4343, device_draw=True)
+    qfull = arrms.fused_allreduce_rms_norm_quant(qinp["partials"], qinp["residual"],
+                                                 qinp["weight"], 1e-6, 128, gemma=gemma)
+    n = 256
+    qpart = arrms.fused_allreduce_rms_norm_quant([p[:n] for p in qinp["partials"]],
+                                                 qinp["residual"][:n], qinp["weight"], 1e-6,
+                                                 128, gemma=gemma)
+    torch.cuda.synchronize()
+    code = arrms.BF16 if dtype == torch.bfloat16 else arrms.FP16
+    assert arrms.cached_plan(4, 2048, 7168, code).kernel == arrms.KERNEL_SPLIT
+    for a, b in zip(qpart, qfull):
+        if a.dtype == torch.float8_e4m3fn:
+            a, b = a.view(torch.uint8), b.view(torch.uint8)
+        elif a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        else:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b[:n])
+
+
 def test_graph_capture_replays_match_eager():
     wl = WORKLOADS["c2"]
     inp = cuda_inputs(wl, 8)
