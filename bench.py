@@ -8,11 +8,15 @@ Headline workload: the decode-window sweep, W=4 partial buffers of [T, 4096]
 bf16 with Gemma RMSNorm, eps 1e-6, T in {1, 2, 4, 8, 16, 21, 22, 32, 64, 80},
 row-resident kernel.  One step is one pass over the sweep: ten fused calls,
 one per T; the inputs are resident in HBM before the timed region starts.
-Steps are launched from HIP graphs that hold up to G steps each (as a captured
-decode step holds every layer's epilogue).  Any K and W are accepted: the
-warm-up and the timed steps are cut into graphs of G steps and one graph of
-the remainder, all captured before the warm-up; exactly K steps are timed,
-between two device synchronisations, with HIP events on the replaying stream.
+Steps are launched from HIP graphs that hold up to G steps each (default 20,
+200 calls: a captured decode step holds every layer's epilogues, two per
+layer, and each graph launch costs the device a few microseconds once per
+graph; the line reports that cost as graph_launch_us).  Any K and W are
+accepted: the warm-up and the timed steps are cut into graphs of G steps and
+one graph of the remainder, all captured before the warm-up; exactly K steps
+are timed with HIP events on the replaying stream, the start event queued
+behind the last warm-up replay, and the device is synchronised before that
+replay and after the timed steps.
 value = microseconds per fused call (timed region / (10 K)).
 
 Beside the headline, the same sweep is timed
@@ -105,7 +109,7 @@ def parser():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000, help="timed steps (any K >= 1)")
     ap.add_argument("--warmup", type=int, default=200, help="untimed steps before (any W >= 0)")
-    ap.add_argument("--steps-per-graph", type=int, default=10,
+    ap.add_argument("--steps-per-graph", type=int, default=20,
                     help="steps held by one HIP graph (the last graph holds the remainder)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timings on the host")
@@ -712,6 +716,22 @@ def main():
             per_t[str(case[0])] = round(graph_time(torch, one, 20, 2, 100, stream), 3)
         config["per_T_us_per_call"] = per_t
         log(f"[bench]   per-T us/call: {per_t}")
+        # the cost of a graph launch on the device, from the sweep in graphs of
+        # 10 and of 50 steps (100 and 500 calls): each replay adds it once
+        def sweep_steps(n):
+            def launch():
+                for _ in range(n):
+                    for T, inp, pl, norm, res in cases:
+                        arrms.ar_rms_run(pl, inp["partials"], inp["residual"], inp["weight"],
+                                         wl.eps, True, norm, res, stream=stream)
+            return launch
+        by_size = {str(10 * n): round(graph_time(torch, sweep_steps(n), reps, 3, 10 * n, stream), 4)
+                   for n, reps in ((10, 100), (50, 20))}
+        config["us_per_call_by_graph_calls"] = by_size
+        config["graph_launch_us"] = round((by_size["100"] - by_size["500"])
+                                          / (1 / 100 - 1 / 500), 2)
+        log(f"[bench]   per call in graphs of 100 / 500 calls: {by_size}, "
+            f"graph launch {config['graph_launch_us']} us")
         # launch floor on this machine: a one-element torch fill kernel replayed the
         # same way (what any single-kernel call costs before it does any work),
         # and torch's add of two [1, H] rows into a third

@@ -123,8 +123,8 @@ def steps_of(graphs):
 
 
 def test_short_invocation_is_accepted_before_any_gpu_work():
-    """`bench.py --gpus 1 --steps 20 --warmup 5 --check-args` (step counts that
-    are not multiples of the steps per graph): the arguments pass, exactly 20
+    """`bench.py --gpus 1 --steps 20 --warmup 5 --check-args` (a warm-up that
+    is not a multiple of the steps per graph): the arguments pass, exactly 20
     steps are timed after exactly 5 warm-up steps, and torch has not been
     imported by then."""
     r = run_bench("--gpus", "1", "--steps", "20", "--warmup", "5", "--check-args")
